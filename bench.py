@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X.
+
+A step is one moe_layer_forward (routing, histogram/scan/scatter, grouped gate_up +
+SwiGLU, grouped down, weighted combine) over one batch of synthetic tokens whose
+inputs are resident in HBM.  The default workload is the 512-token prefill of a
+Qwen3.6-35B-A3B-shaped layer (d_model 2048, 256 experts top-8 + 1 shared expert,
+d_ff 512, int4 weights with bf16 scale and bias per 64).  Four distinct weight sets
+(455 MB each, more than the 256 MB Infinity Cache) rotate so that every step streams
+its weights from HBM.
+
+Prints one JSON line: value = tokens/s, plus the roofline of the dominant kernel
+(grouped gate_up, timed with HIP events recorded by the library at stage boundaries on
+the layer's stream) and the CPU oracle's rate on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config prefill512|zipf8192|...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, AMD published
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+# counters of a plain copy kernel of known size, read in the same rocprofv3 --pmc runs
+# as the gate_up kernel (KiB per dispatch); None until profiled
+TRAFFIC = {
+    # config: {"fetch_kib": ..., "write_kib": ..., "copy_fetch_kib": ..., "copy_write_kib": ...,
+    #          "copy_bytes": ...}
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="prefill512")
+    ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling PMC byte counters)")
+    return ap.parse_args()
+
+
+def gate_up_algorithmic(cfg, touched_groups):
+    """Bytes and flops the grouped gate_up must move/do at minimum: touched groups' codes +
+    scale + bias (2F x D weights at 0.5625 B each), x read once, activations written."""
+    wbytes = touched_groups * 2 * cfg.F * cfg.D * (4 + 32 / 64) / 8
+    bytes_ = wbytes + cfg.T * cfg.D * 2 + (cfg.k + 1) * cfg.T * cfg.F * 2
+    flops = 2.0 * (cfg.k + 1) * cfg.T * 2 * cfg.F * cfg.D
+    return bytes_, flops
+
+
+def cpu_baseline(cfg, x, router, w):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    if cfg.T <= 512:
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, router, w, cfg.k)
+        dt = time.perf_counter() - t0
+        n, sample = cfg.T, f"the whole {cfg.T}-token layer (routing, all experts, combine), fp64"
+    else:
+        toks = np.random.default_rng(7).integers(0, cfg.T, 128)
+        t0 = time.perf_counter()
+        oracle.moe_out_for_tokens(x, router, w, cfg.k, toks)
+        dt = time.perf_counter() - t0
+        n, sample = len(toks), f"128 sampled tokens of the {cfg.T}-token layer, fp64"
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard by tokens or experts; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_grouped_expert_amd import _lib as L
+    from bit_grouped_expert_amd import device as dev
+    from bit_grouped_expert_amd import workload as wl
+
+    cfg = wl.CONFIGS[args.config]
+    assert torch.cuda.is_available()
+    L.lib()
+    log(f"bench: config {cfg.name} T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F}")
+    x, router = wl.make_activations(cfg, 0)
+    host_w0 = None
+    sets = []
+    for i in range(args.weight_sets):
+        w = wl.make_weights(cfg, wl.layer_seed(i))
+        if i == 0:
+            host_w0 = w
+        sets.append(dev.LayerWeights(w, cfg.E))
+        log(f"bench: weight set {i} uploaded ({sets[-1].nbytes() / 1e6:.1f} MB)")
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        lw = sets[i % len(sets)]
+        L.moe_layer_forward(shp, xd, rd, lw.experts, lw.shared, out, ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: warmup done ({args.warmup} steps)")
+
+    # ---- timed region: exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    # ---- per-stage durations: HIP events recorded by the library on the same stream
+    nst = L.N_STAGE_EVENTS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        lw = sets[i % len(sets)]
+        L.moe_layer_forward_events(shp, xd, rd, lw.experts, lw.shared, out, ws, evs[i],
+                                   stream=stream)
+    torch.cuda.synchronize()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    log("bench: stage ms " + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in stage_ms.items()))
+
+    # touched groups from this run's own group offsets (reporting only)
+    lay = L.moe_workspace_layout(shp)
+    offs = ws[lay.offsets:lay.offsets + 4 * (cfg.E + 2)].cpu().numpy().view(np.int32)
+    touched = int(np.count_nonzero(np.diff(offs[:cfg.E + 1]))) + 1
+    gb, gf = gate_up_algorithmic(cfg, touched)
+    gu_s = stage_ms["gate_up"] * 1e-3
+    if gf / gb < RIDGE:
+        roof = {"bound": "hbm", "achieved": gb / gu_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gf / gu_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    t = TRAFFIC.get(cfg.name)
+    if t:
+        scale_f = t["copy_bytes"] / (t["copy_fetch_kib"] * 1024)
+        scale_w = t["copy_bytes"] / (t["copy_write_kib"] * 1024)
+        roof["traffic"] = t["fetch_kib"] * 1024 * scale_f + t["write_kib"] * 1024 * scale_w
+    else:
+        roof["traffic"] = None
+    roof["kernel"] = "q4_gemm_rows_kernel (grouped gate_up + SwiGLU)"
+    roof["algorithmic_bytes"] = gb
+    roof["algorithmic_flops"] = gf
+    roof["kernel_us"] = gu_s * 1e6
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("bench: copy probe (1 GiB) done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        cpu = cpu_baseline(cfg, x, router, host_w0)
+
+    value = cfg.T / (ms_per_step * 1e-3)
+    line = {
+        "metric": "MoE-layer tokens/sec (T=512 prefill; % of HBM / MFMA roofline)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random-init int4-g64 weights, 4 rotating weight sets)",
+        "config": {"workload": f"{cfg.name}: one MoE layer, T={cfg.T}, d_model={cfg.D}, "
+                               f"{cfg.E} experts top-{cfg.k} + 1 shared, SwiGLU d_ff={cfg.F}, "
+                               "int4 g64 bf16 scale+bias",
+                   "T": cfg.T, "d_model": cfg.D, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.F,
+                   "routing": cfg.routing, "parallelism": "single GPU"},
+        "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "touched_groups": touched,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

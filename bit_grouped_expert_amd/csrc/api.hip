@@ -1,0 +1,359 @@
+// C ABI of libmoeq4: host-side validation, workspace carving and launches.
+// Every entry point validates on the host before it enqueues anything, then
+// enqueues its kernels on the caller's stream and returns without waiting.
+#include <string.h>
+
+#include "../../include/moeq4.h"
+#include "internal.h"
+
+using namespace moeq4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr float kRefineGap = 1e-4f;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->T < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->n_experts < 1 || s->n_experts > 1024 ||
+      s->top_k < 1 || s->top_k > 32 || s->top_k > s->n_experts)
+    return MOE_ERR_SHAPE;
+  if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_SHAPE;
+  const int64_t widest = s->d_model > 2 * (int64_t)s->d_ff ? s->d_model : 2 * (int64_t)s->d_ff;
+  if ((int64_t)(s->top_k + 1) * s->T * widest >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if ((int64_t)s->n_experts * s->d_model * 3 >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// rows per tile of the grouped GEMMs inside the layer: 32 while groups average
+// at most 64 rows, 64 beyond
+int layer_bm(const moe_shape* s) {
+  const int64_t rows = (int64_t)(s->top_k + 1) * s->T;
+  return rows <= 64 * (int64_t)(s->n_experts + 1) ? 32 : 64;
+}
+
+struct Layout {
+  size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
+      tile_count, act, y, total;
+};
+
+Layout make_layout(const moe_shape* s) {
+  const int64_t T = s->T, D = s->d_model, E = s->n_experts, k = s->top_k, F = s->d_ff;
+  const int64_t rows_ext = (k + 1) * T;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.rsplit = take(3 * E * D * 2);
+  L.logits = take(T * E * 4);
+  L.topk_idx = take(T * k * 4);
+  L.topk_w = take(T * k * 4);
+  L.chunk_cnt = take((size_t)n_chunks((int)T) * E * 4);
+  L.offsets = take((E + 2) * 4);
+  L.sorted_tok = take(rows_ext * 4);
+  L.slot_row = take(T * k * 4);
+  L.tiles = take((size_t)max_tiles(rows_ext, (int)E + 1, 32) * sizeof(int4));
+  L.tile_count = take(16);
+  L.act = take(rows_ext * F * 2);
+  L.y = take(rows_ext * D * 2);
+  L.total = o;
+  return L;
+}
+
+bool q4_ok(const moe_q4& w) { return w.q && w.scale && w.bias; }
+bool q4_aligned(const moe_q4& w) {
+  return aligned16(w.q) && aligned16(w.scale) && aligned16(w.bias);
+}
+
+moe_status launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "invalid shape";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return make_layout(shape).total;
+}
+
+moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!layout) return MOE_ERR_NULL;
+  const Layout L = make_layout(shape);
+  layout->topk_idx = L.topk_idx;
+  layout->topk_w = L.topk_w;
+  layout->offsets = L.offsets;
+  layout->sorted_tok = L.sorted_tok;
+  layout->slot_row = L.slot_row;
+  layout->act = L.act;
+  layout->y = L.y;
+  layout->total = L.total;
+  return MOE_OK;
+}
+
+size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total) {
+  if (n_groups < 1 || rows_total < 0) return 0;
+  return align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4)) + kAlign;
+}
+
+static moe_status route_impl(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             hipStream_t stream, float gap) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  if (!x || !router_w || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(topk_idx) || !aligned16(topk_w))
+    return MOE_ERR_ALIGN;
+  const Layout L = make_layout(shape);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  const int T = shape->T, D = shape->d_model, E = shape->n_experts, k = shape->top_k;
+  uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
+  float* logits = at<float>(ws, L.logits);
+  launch_router_split(router_w, Rs, E, D, stream);
+  launch_router_logits(x, Rs, logits, T, D, E, stream);
+  launch_topk(logits, x, router_w, T, D, E, k, gap, topk_idx, topk_w, stream);
+  return launch_status();
+}
+
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return route_impl(shape, x, router_w, topk_idx, topk_w, ws, ws_bytes, stream, kRefineGap);
+}
+
+moe_status moe_route_ex(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                        int32_t* topk_idx, float* topk_w, float refine_gap, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (!(refine_gap >= 0.f)) return MOE_ERR_SHAPE;
+  return route_impl(shape, x, router_w, topk_idx, topk_w, ws, ws_bytes, stream, refine_gap);
+}
+
+static moe_status permute_impl(const moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
+                               int32_t* sorted_tok, int32_t* slot_row, int32_t* chunk_cnt,
+                               int shared_rows, hipStream_t stream) {
+  const int T = shape->T, E = shape->n_experts, k = shape->top_k;
+  const int nch = n_chunks(T);
+  launch_count(topk_idx, T, k, E, chunk_cnt, stream);
+  launch_scan(chunk_cnt, nch, E, offsets, shared_rows, stream);
+  launch_scatter(topk_idx, T, k, E, chunk_cnt, offsets, sorted_tok, slot_row,
+                 shared_rows >= 0 ? T * k : -1, stream);
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
+                       int32_t* sorted_tok, int32_t* slot_row, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !offsets || !sorted_tok || !slot_row) return MOE_ERR_NULL;
+  if (!aligned16(topk_idx) || !aligned16(offsets) || !aligned16(sorted_tok) || !aligned16(slot_row))
+    return MOE_ERR_ALIGN;
+  const Layout L = make_layout(shape);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  if (shape->T == 0) {
+    // empty routing still defines offsets (all zero): a scan over zero chunks
+    launch_scan(at<int32_t>(ws, L.chunk_cnt), 0, shape->n_experts, offsets, -1, stream);
+    return launch_status();
+  }
+  permute_impl(shape, topk_idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt), -1,
+               stream);
+  return launch_status();
+}
+
+moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
+                               const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
+                               const int32_t* offsets, moe_q4 W, int32_t epilogue, uint16_t* C,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_groups < 1 || rows_total < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 ||
+      (epilogue != 0 && epilogue != 1))
+    return MOE_ERR_SHAPE;
+  const int64_t widest = N > K ? N : K;
+  if ((int64_t)rows_total * widest >= ((int64_t)1 << 31) ||
+      (int64_t)a_rows * K >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  if (rows_total == 0) return MOE_OK;
+  if (!A || !offsets || !q4_ok(W) || !C) return MOE_ERR_NULL;
+  if (!aligned16(A) || !aligned16(offsets) || !q4_aligned(W) || !aligned16(C) ||
+      (a_row_index && !aligned16(a_row_index)))
+    return MOE_ERR_ALIGN;
+  const size_t need = moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+
+  const int bm = rows_total <= 64 * (int64_t)n_groups ? 32 : 64;
+  const int64_t bound = max_tiles(rows_total, n_groups, bm);
+  int4* tiles = at<int4>(ws, 0);
+  int32_t* tile_count =
+      at<int32_t>(ws, align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4)));
+  launch_build_tiles(offsets, n_groups, rows_total, bm, tiles, tile_count, stream);
+
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.a_row_index = a_row_index;
+  p.a_rows = a_rows;
+  p.main = Q4Ptrs{W.q, W.scale, W.bias};
+  p.n_main = n_groups;
+  p.last = p.main;
+  p.N = N;
+  p.K = K;
+  p.C = C;
+  p.ldc = epilogue == 1 ? N / 2 : N;
+  p.tiles = tiles;
+  p.tile_count = tile_count;
+  launch_gemm_q4(p, bm, epilogue == 1, bound, stream);
+  return launch_status();
+}
+
+moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const int32_t* slot_row,
+                       const float* topk_w, const uint16_t* shared_out, uint16_t* out,
+                       hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  if (!y_sorted || !slot_row || !topk_w || !out) return MOE_ERR_NULL;
+  if (!aligned16(y_sorted) || !aligned16(slot_row) || !aligned16(topk_w) || !aligned16(out) ||
+      (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_ALIGN;
+  const int T = shape->T, D = shape->d_model, k = shape->top_k;
+  launch_combine(y_sorted, (int64_t)T * k, slot_row, topk_w, shared_out, out, T, D, k, stream);
+  return launch_status();
+}
+
+static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                             const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
+                             void* ws, size_t ws_bytes, hipEvent_t* events, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  if (!x || !router_w || !experts || !out) return MOE_ERR_NULL;
+  if (!q4_ok(experts->gate_up) || !q4_ok(experts->down)) return MOE_ERR_NULL;
+  if (shared && (!q4_ok(shared->gate_up) || !q4_ok(shared->down))) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(out) ||
+      !q4_aligned(experts->gate_up) || !q4_aligned(experts->down) ||
+      (shared && (!q4_aligned(shared->gate_up) || !q4_aligned(shared->down))))
+    return MOE_ERR_ALIGN;
+  const Layout L = make_layout(shape);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+
+  const int T = shape->T, D = shape->d_model, E = shape->n_experts, k = shape->top_k,
+            F = shape->d_ff;
+  const bool has_shared = shared != nullptr;
+  const int n_groups = E + (has_shared ? 1 : 0);
+  const int rows = T * k + (has_shared ? T : 0);
+
+  int32_t* idx = at<int32_t>(ws, L.topk_idx);
+  float* wts = at<float>(ws, L.topk_w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted_tok = at<int32_t>(ws, L.sorted_tok);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  int4* tiles = at<int4>(ws, L.tiles);
+  int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  uint16_t* act = at<uint16_t>(ws, L.act);
+  uint16_t* y = at<uint16_t>(ws, L.y);
+
+  auto mark = [&](int i) {
+    if (events && events[i]) hipEventRecord(events[i], stream);
+  };
+  // routing
+  mark(0);
+  uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
+  float* logits = at<float>(ws, L.logits);
+  launch_router_split(router_w, Rs, E, D, stream);
+  launch_router_logits(x, Rs, logits, T, D, E, stream);
+  launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
+  mark(1);
+  // histogram, scan, scatter (+ identity rows of the shared group), tile map
+  permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
+               has_shared ? T : -1, stream);
+  const int bm = layer_bm(shape);
+  const int64_t bound = max_tiles(rows, n_groups, bm);
+  launch_build_tiles(offsets, n_groups, rows, bm, tiles, tile_count, stream);
+  mark(2);
+
+  // gate_up + SwiGLU: x rows gathered through sorted_tok -> act [rows, F]
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = x;
+  p.a_row_index = sorted_tok;
+  p.a_rows = T;
+  p.main = Q4Ptrs{experts->gate_up.q, experts->gate_up.scale, experts->gate_up.bias};
+  p.n_main = E;
+  p.last = has_shared ? Q4Ptrs{shared->gate_up.q, shared->gate_up.scale, shared->gate_up.bias}
+                      : p.main;
+  p.N = 2 * F;
+  p.K = D;
+  p.C = act;
+  p.ldc = F;
+  p.tiles = tiles;
+  p.tile_count = tile_count;
+  launch_gemm_q4(p, bm, true, bound, stream);
+  mark(3);
+
+  // down: act rows in order -> y [rows, D]
+  p.A = act;
+  p.a_row_index = nullptr;
+  p.a_rows = rows;
+  p.main = Q4Ptrs{experts->down.q, experts->down.scale, experts->down.bias};
+  p.last = has_shared ? Q4Ptrs{shared->down.q, shared->down.scale, shared->down.bias} : p.main;
+  p.N = D;
+  p.K = F;
+  p.C = y;
+  p.ldc = D;
+  launch_gemm_q4(p, bm, false, bound, stream);
+  mark(4);
+
+  // combine with the shared expert (rows T*k.. of y)
+  launch_combine(y, (int64_t)T * k, slot_row, wts, has_shared ? y + (int64_t)T * k * D : nullptr,
+                 out, T, D, k, stream);
+  mark(5);
+  return launch_status();
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                             const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_impl(shape, x, router_w, experts, shared, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_events(const moe_shape* shape, const uint16_t* x,
+                                    const float* router_w, const moe_q4_ffn* experts,
+                                    const moe_q4_ffn* shared, uint16_t* out, void* ws,
+                                    size_t ws_bytes, hipEvent_t* events, hipStream_t stream) {
+  return layer_impl(shape, x, router_w, experts, shared, out, ws, ws_bytes, events, stream);
+}
+
+}  // extern "C"

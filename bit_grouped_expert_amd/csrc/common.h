@@ -1,0 +1,75 @@
+// Device helpers shared by the gfx950 kernels of the int4-g64 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeq4 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA bf16 operand (8 per lane)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;      // 16x16 MFMA accumulator (4 per lane)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;   // weights per (scale, bias) pair
+
+// bf16 bits (low 16 bits of `b`) -> fp32, exact.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+// bf16 bits in the high 16 bits of `b` -> fp32, exact.
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t b) { return __uint_as_float(b & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Butterfly exchange with the lane `lane ^ mask` (ds_bpermute based).
+__device__ __forceinline__ uint32_t xor_u32(uint32_t v, int mask) {
+  int src = (lane_id() ^ mask) << 2;
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v);
+}
+__device__ __forceinline__ uint64_t xor_u64(uint64_t v, int mask) {
+  uint32_t lo = xor_u32((uint32_t)v, mask), hi = xor_u32((uint32_t)(v >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double xor_f64(double v, int mask) {
+  return __longlong_as_double((long long)xor_u64((uint64_t)__double_as_longlong(v), mask));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Sum over the wave in a fixed butterfly order (every lane gets the same bits).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += xor_f64(v, m);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t ldg_u32(const void* p) {
+  return __builtin_nontemporal_load((const uint32_t*)p);
+}
+
+}  // namespace moeq4

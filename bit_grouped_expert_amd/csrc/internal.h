@@ -1,0 +1,62 @@
+// Internal launchers and workspace layout of libmoeq4 (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq4 {
+
+// ---------------------------------------------------------------- routing
+void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t s);
+void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
+                          hipStream_t s);
+void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
+                 float tau, int32_t* idx, float* w, hipStream_t s);
+
+// ---------------------------------------------------------------- permutation
+constexpr int kChunkTokens = 256;  // tokens per histogram / scatter chunk
+inline int n_chunks(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
+void launch_count(const int32_t* idx, int T, int k, int E, int32_t* chunk_cnt, hipStream_t s);
+void launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
+                 hipStream_t s);
+void launch_scatter(const int32_t* idx, int T, int k, int E, const int32_t* chunk_base,
+                    const int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, int shared_base,
+                    hipStream_t s);
+
+// ---------------------------------------------------------------- grouped GEMM
+struct Q4Ptrs {
+  const uint32_t* q;
+  const uint16_t* s;
+  const uint16_t* b;
+};
+
+struct GemmParams {
+  const uint16_t* A;          // bf16 [a_rows, K]
+  const int32_t* a_row_index; // nullable: identity
+  int32_t a_rows;
+  Q4Ptrs main;                // groups 0..n_main-1, contiguous
+  int32_t n_main;
+  Q4Ptrs last;                // group n_main (if any)
+  int32_t N, K;
+  uint16_t* C;                // bf16 [rows, ldc]
+  int32_t ldc;
+  const int4* tiles;          // (group, row0, rows, 0)
+  const int32_t* tile_count;
+  int32_t n_slices;
+};
+
+inline int64_t max_tiles(int64_t rows_total, int n_groups, int bm) {
+  return (rows_total + bm - 1) / bm + n_groups;
+}
+void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
+                        int32_t* tile_count, hipStream_t s);
+// bm: 32 or 64 rows per tile.  Grid = max_tiles(rows_total, n_groups, bm) * n_slices.
+void launch_gemm_q4(GemmParams p, int bm, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
+int gemm_q4_slices(int N, bool swiglu);
+
+// ---------------------------------------------------------------- combine
+void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
+                    const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);
+
+}  // namespace moeq4

@@ -1,0 +1,191 @@
+// Histogram, prefix scan and stable scatter of routed (token, slot) pairs into
+// contiguous per-expert groups, plus the tile map of the grouped GEMM.
+//
+// Pages: MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference
+// engine for Qwen3.6-35B-A3B on Apple Silicon", body paragraph 4 (routing gives
+// uneven expert groups) and paragraph 6 (the routing histogram, prefix scan,
+// scatter and block map stay on the GPU, with no CPU synchronisation inside the
+// MoE layer).  Everything here is integer work sized from host-known bounds; the
+// host never reads a count back.
+//
+// Stability: rows of an expert hold its tokens in ascending token order.  Tokens
+// are cut into chunks of 256; a chunk's base row for expert e is offsets[e] plus
+// the number of earlier-chunk pairs routed to e (column scan of per-chunk
+// counts); inside a chunk each wavefront of 64 tokens sets one bit per token in a
+// 64-bit mask per expert, and a token's rank is the popcount of the masks of the
+// lower waves plus the bits of lower lanes in its own wave.
+#include "common.h"
+#include "internal.h"
+
+namespace moeq4 {
+
+// ---------------------------------------------------------------------------- count
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                    int E, int32_t* __restrict__ chunk_cnt) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kChunkTokens + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+void launch_count(const int32_t* idx, int T, int k, int E, int32_t* chunk_cnt, hipStream_t s) {
+  hipLaunchKernelGGL(count_kernel, dim3(n_chunks(T)), dim3(256), E * sizeof(int32_t), s, idx, T, k,
+                     E, chunk_cnt);
+}
+
+// ---------------------------------------------------------------------------- block scan
+// Exclusive scan of one int per thread over a 1024-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    int sv = wsum[w];
+    if (w < wave) base += sv;
+    tot += sv;
+  }
+  __syncthreads();  // wsum may be reused by the next call
+  *total = tot;
+  return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------- scan
+// One workgroup of 1024 threads.  chunk_cnt [nchunks, E] is replaced by each
+// chunk's exclusive base per expert; offsets[0..E] is the exclusive scan of the
+// expert totals; if shared_rows >= 0, offsets[E+1] = offsets[E] + shared_rows.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ chunk_cnt, int nchunks,
+                                                    int E, int32_t* __restrict__ offsets,
+                                                    int shared_rows) {
+  const int e = threadIdx.x;
+  int running = 0;
+  if (e < E) {
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = chunk_cnt[(int64_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        chunk_cnt[(int64_t)(c + i) * E + e] = running;
+        running += v[i];
+      }
+    }
+    for (; c < nchunks; ++c) {
+      int v = chunk_cnt[(int64_t)c * E + e];
+      chunk_cnt[(int64_t)c * E + e] = running;
+      running += v;
+    }
+  }
+  int total;
+  const int excl = block_exclusive_scan_1024(e < E ? running : 0, &total);
+  if (e < E) offsets[e] = excl;
+  if (threadIdx.x == 0) {
+    offsets[E] = total;
+    if (shared_rows >= 0) offsets[E + 1] = total + shared_rows;
+  }
+}
+
+void launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_cnt, nchunks, E, offsets,
+                     shared_rows);
+}
+
+// ---------------------------------------------------------------------------- scatter
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_tok,
+    int32_t* __restrict__ slot_row, int shared_base) {
+  extern __shared__ unsigned long long masks[];  // [4 waves][E]
+  for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kChunkTokens + threadIdx.x;
+  const unsigned long long bit = 1ull << lane;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const int32_t* base = chunk_base + (int64_t)blockIdx.x * E;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      int32_t row = -1;
+      if (e >= 0 && e < E) {
+        int rank = __popcll(masks[wave * E + e] & (bit - 1ull));
+        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+        row = offsets[e] + base[e] + rank;
+        if (row >= 0 && row < T * k) sorted_tok[row] = t;  // always true for consistent counts
+        else row = -1;
+      }
+      slot_row[(int64_t)t * k + j] = row;
+    }
+    if (shared_base >= 0) sorted_tok[shared_base + t] = t;
+  }
+}
+
+void launch_scatter(const int32_t* idx, int T, int k, int E, const int32_t* chunk_base,
+                    const int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, int shared_base,
+                    hipStream_t s) {
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks(T)), dim3(256),
+                     4 * E * sizeof(unsigned long long), s, idx, T, k, E, chunk_base, offsets,
+                     sorted_tok, slot_row, shared_base);
+}
+
+// ---------------------------------------------------------------------------- tile map
+// One workgroup of 1024 threads: tiles of at most `bm` rows over every group,
+// group by group, as (group, first row, rows, 0).  Offsets are clamped into
+// [0, rows_total] so that no tile leaves C, and at most `cap` tiles are written
+// (cap = the bound the grid was sized with), so malformed offsets cannot
+// overrun the tile array.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                           int n_groups, int rows_total, int bm,
+                                                           int4* __restrict__ tiles, int cap,
+                                                           int32_t* __restrict__ tile_count) {
+  int running = 0;
+  for (int g0 = 0; g0 < n_groups; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int lo = 0, n = 0;
+    if (g < n_groups) {
+      lo = min(max(offsets[g], 0), rows_total);
+      int hi = min(max(offsets[g + 1], lo), rows_total);
+      n = hi - lo;
+    }
+    const int nt = (n + bm - 1) / bm;
+    int total;
+    const int first = running + block_exclusive_scan_1024(nt, &total);
+    for (int i = 0; i < nt && first + i < cap; ++i)
+      tiles[first + i] = make_int4(g, lo + i * bm, min(bm, n - i * bm), 0);
+    running += total;
+  }
+  if (threadIdx.x == 0) *tile_count = min(running, cap);
+}
+
+void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
+                        int32_t* tile_count, hipStream_t s) {
+  const int cap = (int)max_tiles(rows_total, n_groups, bm);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, n_groups, rows_total,
+                     bm, tiles, cap, tile_count);
+}
+
+}  // namespace moeq4

@@ -1,0 +1,266 @@
+// Router of the MoE layer: fp32 logits, top-k selection and routing weights.
+//
+// Pages: MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference
+// engine for Qwen3.6-35B-A3B on Apple Silicon", body paragraph 4 (a router
+// scores 256 experts and picks eight, plus a shared expert that sees every
+// token).  The weighting (softmax over the selected logits) and the tie rule
+// (equal logits go to the lower expert id) are readings; the pages state neither.
+//
+// Logits.  L = x R^T with x bf16 [T, D] and R fp32 [E, D].  R is split once per
+// call into three bf16 planes R = R0 + R1 + R2 (each the round-to-nearest-even of
+// the remainder), which carries R's full 24-bit significand.  A product of a bf16
+// x with a bf16 plane is exact in fp32, so three bf16 MFMAs with fp32
+// accumulation give fp32-FMA accuracy at bf16 matrix-core speed.
+//
+// Selection.  One wavefront per token ranks the logits by a 64-bit key
+// (order-preserving float bits, then the complemented expert id so equal logits
+// rank the lower id higher) and extracts the k+1 best.  If the k-th and (k+1)-th
+// fp32 logits are closer than `tau`, every expert whose fp32 logit is at least
+// L_(k+1) - tau is rescored exactly in fp64 (bf16 x fp32 products are exact in
+// fp64) and the top k of those, by fp64 logit, are chosen.  Any expert outside
+// that set has a true logit below k+1 candidates' as long as the fp32 error is
+// under tau/2, so the selection equals the exact (fp64) top-k.
+#include "common.h"
+#include "internal.h"
+
+namespace moeq4 {
+
+// ---------------------------------------------------------------------------- split
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ R,
+                                                           uint16_t* __restrict__ Rs, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float r = R[i];
+    uint16_t h0 = to_bf16(r);
+    float r1 = r - bf16lo_to_f32(h0);
+    uint16_t h1 = to_bf16(r1);
+    float r2 = r1 - bf16lo_to_f32(h1);
+    uint16_t h2 = to_bf16(r2);
+    Rs[i] = h0;
+    Rs[n + i] = h1;
+    Rs[2 * n + i] = h2;
+  }
+}
+
+void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t s) {
+  int64_t n = (int64_t)E * D;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(router_split_kernel, dim3(blocks), dim3(256), 0, s, R, Rs, n);
+}
+
+// ---------------------------------------------------------------------------- logits
+// Workgroup tile: TM tokens x 64 experts; wave w owns experts e0 + 16w .. +15.
+// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (l % 16) and the
+// eight k-slots 8*(l/16)..+7; the accumulator holds rows 4*(l/16)+i, column l%16.
+template <int TM>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ Rs,
+                                                            float* __restrict__ L, int T, int D,
+                                                            int E) {
+  constexpr int NT = TM / 16;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int m = l & 15, q = l >> 4;
+  const int t0 = blockIdx.x * TM;
+  const int e0 = blockIdx.y * 64 + wave * 16;
+  if (e0 >= E) return;  // this kernel has no barriers
+  const int e = e0 + m;
+  const bool ev = e < E;
+  const int64_t plane = (int64_t)E * D;
+  const uint16_t* rb = Rs + (int64_t)(ev ? e : 0) * D + 8 * q;
+  const uint16_t* xa[NT];
+  bool tv[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    int t = t0 + 16 * i + m;
+    tv[i] = t < T;
+    xa[i] = x + (int64_t)(tv[i] ? t : 0) * D + 8 * q;
+  }
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    u32x4_t b0 = ev ? *(const u32x4_t*)(rb + k0) : zero;
+    u32x4_t b1 = ev ? *(const u32x4_t*)(rb + plane + k0) : zero;
+    u32x4_t b2 = ev ? *(const u32x4_t*)(rb + 2 * plane + k0) : zero;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      u32x4_t a = tv[i] ? *(const u32x4_t*)(xa[i] + k0) : zero;
+      acc[i] = mfma16x16x32(a, b0, acc[i]);
+      acc[i] = mfma16x16x32(a, b1, acc[i]);
+      acc[i] = mfma16x16x32(a, b2, acc[i]);
+    }
+  }
+  if (!ev) return;
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int t = t0 + 16 * i + 4 * q + r;
+      if (t < T) L[(int64_t)t * E + e] = acc[i][r];
+    }
+}
+
+void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
+                          hipStream_t s) {
+  dim3 block(256);
+  if (T >= 2048) {
+    dim3 grid((T + 63) / 64, (E + 63) / 64);
+    hipLaunchKernelGGL(router_logits_kernel<64>, grid, block, 0, s, x, Rs, L, T, D, E);
+  } else {
+    dim3 grid((T + 15) / 16, (E + 63) / 64);
+    hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, 0, s, x, Rs, L, T, D, E);
+  }
+}
+
+// ---------------------------------------------------------------------------- top-k
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_bits(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ uint64_t ordered_bits64(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// (value, expert) pair order: larger value first, then lower expert id.
+struct Cand {
+  double v;
+  int e;
+};
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  return a.v > b.v || (a.v == b.v && a.e < b.e);
+}
+
+// One wavefront per token; E <= 64 * MAXC.
+template <int MAXC>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
+                                                   const uint16_t* __restrict__ x,
+                                                   const float* __restrict__ R, int T, int D,
+                                                   int E, int k, float tau,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // no barriers below
+  const float* Lt = L + (int64_t)t * E;
+
+  float val[MAXC];
+  uint64_t key[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    int e = c * 64 + lane;
+    val[c] = e < E ? Lt[e] : 0.f;
+    key[c] = e < E ? rank_key(val[c], e) : 0ull;
+  }
+
+  // lane j keeps the j-th selection
+  int my_e = -1;
+  float my_v = 0.f;
+  const int nsel = (k + 1 < E) ? k + 1 : E;
+  for (int j = 0; j < nsel; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) best = key[c] > best ? key[c] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const float v = unordered_bits((uint32_t)(best >> 32));
+    if (lane == j) {
+      my_e = e;
+      my_v = v;
+    }
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c)
+        if (c == (e >> 6)) key[c] = 0ull;
+    }
+  }
+
+  if (k < E) {
+    const float vk = __shfl(my_v, k - 1);
+    const float vk1 = __shfl(my_v, k);
+    if (vk - vk1 < tau) {
+      // exact rescoring of every expert within tau below the (k+1)-th logit
+      const float thr = vk1 - tau;
+      double exact[MAXC];
+      bool cand[MAXC];
+      const uint16_t* xt = x + (int64_t)t * D;
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = c * 64 + lane;
+        cand[c] = e < E && val[c] >= thr;
+        exact[c] = 0.0;
+        uint64_t mask = __ballot(cand[c]);
+        while (mask) {
+          const int b = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const float* Re = R + (int64_t)(c * 64 + b) * D;
+          double s = 0.0;
+          for (int d = lane; d < D; d += 64)
+            s += (double)bf16lo_to_f32(xt[d]) * (double)Re[d];
+          s = wave_sum_f64(s);
+          if (lane == b) exact[c] = s;
+        }
+      }
+      // top-k of the candidates by (fp64 logit desc, expert id asc)
+      for (int j = 0; j < k; ++j) {
+        Cand best{-__builtin_inf(), 0x7FFFFFFF};
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          Cand cc{exact[c], c * 64 + lane};
+          if (cand[c] && better(cc, best)) best = cc;
+        }
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) {
+          Cand o;
+          o.v = xor_f64(best.v, msk);
+          o.e = (int)xor_u32((uint32_t)best.e, msk);
+          if (better(o, best)) best = o;
+        }
+        if (best.e >= E) best.e = 0;  // only with NaN logits (fewer than k candidates)
+        if (lane == j) {
+          my_e = best.e;
+          my_v = Lt[best.e];
+        }
+        if ((best.e & 63) == lane) {
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c)
+            if (c == (best.e >> 6)) cand[c] = false;
+        }
+      }
+    }
+  }
+
+  // softmax over the k selected fp32 logits
+  const bool mine = lane < k;
+  float mx = mine ? my_v : -__builtin_inff();
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+  const float z = mine ? __expf(my_v - mx) : 0.f;
+  float sum = z;
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk);
+  if (mine) {
+    idx_out[(int64_t)t * k + lane] = my_e;
+    w_out[(int64_t)t * k + lane] = z / sum;
+  }
+}
+
+void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
+                 float tau, int32_t* idx, float* w, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+}
+
+}  // namespace moeq4

@@ -1,0 +1,200 @@
+/*
+ * moeq4.h -- C ABI of an MI355X (gfx950) mixture-of-experts layer with
+ * groupwise-affine 4-bit expert weights.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [MTP] MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference
+ *         engine for Qwen3.6-35B-A3B on Apple Silicon", body paragraphs 4-7.
+ *   [GF]  globalfeed.ai, "Perplexity open sources Lily, a Rust and Metal
+ *         inference engine for Apple Silicon", sections "Requirements and model
+ *         layout" and "Measurements".
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are row-major.  bf16 values travel as their raw uint16 bits.
+ *   - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
+ *     comment says otherwise; the caller owns every buffer.  The library
+ *     allocates nothing, keeps no pointer after a call returns and has no
+ *     mutable global state, so calls on different streams are thread-safe.
+ *   - Every compute call only enqueues work on `stream` (NULL = the legacy
+ *     default stream) and never waits for the device; buffers must stay valid
+ *     until the stream has passed the call.  No host synchronisation happens
+ *     inside a call ([MTP] para. 6: routing stays on the GPU with no CPU sync
+ *     inside the MoE layer).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     nonzero status means nothing was enqueued.  MOE_ERR_LAUNCH reports a
+ *     launch failure seen by hipGetLastError (kernels already enqueued by the
+ *     same call may still run).  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Outputs must not alias inputs.  NaN/Inf inputs give unspecified results.
+ *   - Required alignment: 16 bytes for every pointer.
+ *
+ * Weight format ([MTP] para. 5; [GF] "Requirements and model layout": 4-bit
+ * weights, every group of 64 sharing one bf16 scale and one bf16 bias):
+ *   A weight matrix W has N output rows and K inputs (K % 64 == 0).
+ *     q     uint32 [groups, N, K/8]   eight 4-bit codes per word; nibble j
+ *                                      (bits 4j..4j+3) of word w is input 8w+j
+ *     scale bf16   [groups, N, K/64]
+ *     bias  bf16   [groups, N, K/64]
+ *   w[n][c] = q[n][c] * scale[n][c/64] + bias[n][c/64]   (q unsigned, 0..15)
+ *   An expert FFN is SwiGLU: gate_up has N = 2F (rows 0..F-1 gate, F..2F-1 up)
+ *   and K = D; down has N = D and K = F.
+ */
+#ifndef MOEQ4_H
+#define MOEQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of range or breaks a divisibility rule */
+  MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 4, /* the workspace is NULL or smaller than required */
+  MOE_ERR_LAUNCH = 5,    /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_DEVICE = 6     /* no usable gfx950 device / device query failed */
+} moe_status;
+
+/* Layer shape.  T tokens, D = d_model, E routed experts, k experts per token,
+ * F = expert d_ff.  Rules: 0 <= T; D % 64 == 0; F % 64 == 0; 1 <= E <= 1024;
+ * 1 <= k <= min(E, 32); (k+1) * T * max(D, 2F) < 2^31. */
+typedef struct {
+  int32_t T, d_model, n_experts, top_k, d_ff;
+} moe_shape;
+
+/* One packed 4-bit weight tensor (format above). */
+typedef struct {
+  const uint32_t* q;
+  const uint16_t* scale;
+  const uint16_t* bias;
+} moe_q4;
+
+/* The weights of a set of SwiGLU experts, stored contiguously group after group. */
+typedef struct {
+  moe_q4 gate_up; /* N = 2F, K = D */
+  moe_q4 down;    /* N = D,  K = F */
+} moe_q4_ffn;
+
+/* Byte offsets of the intermediates moe_layer_forward leaves in its workspace
+ * (valid after the stream has passed the call, until the workspace is reused). */
+typedef struct {
+  size_t topk_idx;   /* int32 [T, k]   selected experts, descending logit */
+  size_t topk_w;     /* fp32  [T, k]   routing weights */
+  size_t offsets;    /* int32 [E + 2]  group row offsets; [E+1] = (k+1)T (shared group) */
+  size_t sorted_tok; /* int32 [(k+1)T] token of each permuted row (tail: 0..T-1) */
+  size_t slot_row;   /* int32 [T, k]   permuted row of pair (t, j) */
+  size_t act;        /* bf16  [(k+1)T, F] SwiGLU activations, permuted rows */
+  size_t y;          /* bf16  [(k+1)T, D] expert outputs; rows kT.. = shared expert */
+  size_t total;      /* == moe_workspace_bytes */
+} moe_ws_layout;
+
+/* Human-readable name of a status (static string; never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* Workspace bytes moe_layer_forward needs for `shape`; this also covers
+ * moe_route and moe_permute.  Host-only, pure; 0 if the shape is invalid. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Fills `layout` for `shape`.  Host-only. */
+moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout);
+
+/* Workspace bytes moe_grouped_gemm_q4 needs (its tile map).  Host-only, pure. */
+size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total);
+
+/* Router: L = x R^T in fp32 (bf16 x split-exact against a three-way bf16 split
+ * of R), top-k by descending logit with exact ties to the lower expert id;
+ * when the k-th and (k+1)-th fp32 logits are closer than 1e-4 the logits of
+ * every expert within 1e-4 of the boundary are recomputed exactly in fp64 and
+ * the selection is redone.  Weights: softmax over the k selected logits.
+ * [MTP] para. 4 (a router scores 256 experts and picks eight).
+ *   x        bf16 [T, D];  router_w fp32 [E, D]
+ *   topk_idx int32 [T, k] (descending logit);  topk_w fp32 [T, k]
+ *   ws       >= moe_workspace_bytes(shape) bytes of scratch (caller-owned). */
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* moe_route with an explicit near-tie threshold (moe_route uses 1e-4).  A larger
+ * refine_gap sends more tokens through the exact fp64 rescoring (for testing);
+ * refine_gap must be >= 0 (else MOE_ERR_SHAPE). */
+moe_status moe_route_ex(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                        int32_t* topk_idx, float* topk_w, float refine_gap, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Histogram, exclusive prefix scan and stable scatter of the (token, slot)
+ * pairs into contiguous per-expert groups ([MTP] paras. 4 and 6: uneven expert
+ * groups; histogram, prefix scan and scatter stay on the GPU).
+ *   topk_idx   int32 [T, k]; the k experts of a token must be distinct (else
+ *              rows are unspecified, though always inside their group);
+ *              entries outside [0, E) are ignored (their slot_row is set to -1
+ *              and they are not counted)
+ *   offsets    int32 [E + 1]: rows of expert e are offsets[e]..offsets[e+1]-1
+ *   sorted_tok int32 [T*k]: token of each permuted row, ascending within a group
+ *   slot_row   int32 [T*k]: slot_row[t*k + j] = permuted row of pair (t, j)
+ *   ws         >= moe_workspace_bytes(shape) bytes. */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
+                       int32_t* sorted_tok, int32_t* slot_row, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Grouped GEMM over 4-bit weights ([MTP] para. 5: the 4-bit weights are
+ * reconstructed tile by tile inside the grouped GEMM with fp32 accumulation,
+ * never expanded in memory).  For each group g and row r in
+ * offsets[g]..offsets[g+1]-1:
+ *   H[r] = A[row(r)] W_g^T   (fp32),  row(r) = a_row_index ? a_row_index[r] : r
+ *   epilogue 0: C[r][n] = bf16(H[r][n]),            C is [rows_total, N]
+ *   epilogue 1: C[r][f] = bf16(silu(H[r][f]) * H[r][N/2 + f]), C is [rows_total, N/2]
+ *   n_groups   >= 1;  N % 64 == 0;  K % 64 == 0;  rows_total >= 0
+ *   A          bf16 [a_rows, K]; rows whose index is outside [0, a_rows) read as zero
+ *   offsets    int32 [n_groups + 1] on the device, non-decreasing from 0;
+ *              values are clamped to [0, rows_total]; C rows outside every
+ *              group are not written
+ *   W          q [n_groups, N, K/8], scale/bias [n_groups, N, K/64]
+ *   ws         >= moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total). */
+moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
+                               const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
+                               const int32_t* offsets, moe_q4 W, int32_t epilogue,
+                               uint16_t* C, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine: out[t] = bf16( S[t] + sum_j topk_w[t][j] * Y[slot_row[t*k+j]] ),
+ * summed in fp32 (S = shared_out, or 0 when NULL).  slot_row entries outside
+ * [0, T*k) are skipped.
+ *   y_sorted bf16 [T*k, D]; slot_row int32 [T*k]; topk_w fp32 [T*k];
+ *   shared_out bf16 [T, D] or NULL; out bf16 [T, D]. */
+moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const int32_t* slot_row,
+                       const float* topk_w, const uint16_t* shared_out, uint16_t* out,
+                       hipStream_t stream);
+
+/* The whole layer on one stream with no host synchronisation: route, permute,
+ * grouped gate_up + SwiGLU over the E routed groups plus the shared expert as
+ * one more group covering all T rows, grouped down, weighted combine.
+ *   x bf16 [T, D]; router_w fp32 [E, D];
+ *   experts: E groups (q [E, 2F, D/8] ... as in the weight format);
+ *   shared: one group, or NULL for no shared expert; out bf16 [T, D];
+ *   ws >= moe_workspace_bytes(shape) bytes; its layout is moe_workspace_layout. */
+moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                             const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward that also records caller-created HIP events on `stream` at
+ * the stage boundaries, for per-stage timing: events[0] before routing,
+ * [1] after routing (logits, top-k), [2] after the permutation and tile map,
+ * [3] after the grouped gate_up + SwiGLU, [4] after the grouped down,
+ * [5] after the combine.  `events` may be NULL and entries may be NULL
+ * (skipped).  Same validation and results as moe_layer_forward. */
+#define MOE_N_STAGE_EVENTS 6
+moe_status moe_layer_forward_events(const moe_shape* shape, const uint16_t* x,
+                                    const float* router_w, const moe_q4_ffn* experts,
+                                    const moe_q4_ffn* shared, uint16_t* out, void* ws,
+                                    size_t ws_bytes, hipEvent_t* events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ4_H */

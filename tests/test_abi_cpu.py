@@ -1,0 +1,148 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every entry point
+include/moeq4.h declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from bit_grouped_expert_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq4.h")
+
+A = 0x10000          # an aligned fake device address (never dereferenced: every call below fails
+B = 0x20000          # validation on the host first)
+MIS = 0x10008        # 8-byte aligned only
+BIG = 1 << 40
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoeq4.so is not built (python -m bit_grouped_expert_amd.build)")
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L._SIGS), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert L.status_string(s)
+    assert L.status_string(99) == "unknown status"
+
+
+def shp(T=512, D=2048, E=256, k=8, F=512):
+    return L.shape(T, D, E, k, F)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(T=-1), dict(D=0), dict(D=100), dict(F=96), dict(E=0), dict(E=1025), dict(k=0),
+    dict(k=33), dict(E=4, k=5), dict(T=1 << 20), dict(T=100000, D=4096),
+])
+def test_shape_rules(lib, bad):
+    s = shp(**bad)
+    assert L.moe_workspace_bytes(s) == 0
+    assert lib.moe_layer_forward(C.byref(s), A, A, C.byref(L.moe_q4_ffn()), None, A, A, BIG, None) \
+        == L.MOE_ERR_SHAPE
+    assert lib.moe_route(C.byref(s), A, A, A, A, A, BIG, None) == L.MOE_ERR_SHAPE
+
+
+def test_workspace_bytes_monotone_and_layout(lib):
+    prev = 0
+    for T in [0, 1, 4, 16, 255, 256, 257, 512, 4096, 8192, 32768]:
+        s = shp(T=T)
+        n = L.moe_workspace_bytes(s)
+        assert n >= prev
+        prev = n
+        lay = L.moe_workspace_layout(s)
+        offs = [lay.topk_idx, lay.topk_w, lay.offsets, lay.sorted_tok, lay.slot_row, lay.act, lay.y]
+        assert all(o % 256 == 0 for o in offs)
+        assert offs == sorted(offs) and lay.total == n
+        assert lay.y + (9 * T) * 2048 * 2 <= n
+    assert L.moe_grouped_gemm_q4_workspace_bytes(0, 10) == 0
+    assert L.moe_grouped_gemm_q4_workspace_bytes(257, 4608) >= (4608 // 32 + 257) * 16
+
+
+def ffn(q=A, s=A, b=A):
+    return L.q4_ffn(L.q4(q, s, b), L.q4(q, s, b))
+
+
+def test_layer_forward_validation(lib):
+    s = shp()
+    need = L.moe_workspace_bytes(s)
+    e, sh = ffn(), ffn()
+    f = lambda *a: lib.moe_layer_forward(*a)  # noqa: E731
+    assert f(None, A, A, C.byref(e), C.byref(sh), A, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), 0, A, C.byref(e), C.byref(sh), A, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), A, A, None, C.byref(sh), A, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), A, A, C.byref(ffn(s=0)), C.byref(sh), A, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), A, A, C.byref(e), C.byref(ffn(b=0)), A, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), A, A, C.byref(e), C.byref(sh), 0, A, need, None) == L.MOE_ERR_NULL
+    assert f(C.byref(s), MIS, A, C.byref(e), C.byref(sh), A, A, need, None) == L.MOE_ERR_ALIGN
+    assert f(C.byref(s), A, A, C.byref(ffn(q=MIS)), C.byref(sh), A, A, need, None) == L.MOE_ERR_ALIGN
+    assert f(C.byref(s), A, A, C.byref(e), C.byref(sh), A, 0, need, None) == L.MOE_ERR_WORKSPACE
+    assert f(C.byref(s), A, A, C.byref(e), C.byref(sh), A, A, need - 1, None) == L.MOE_ERR_WORKSPACE
+    assert f(C.byref(s), A, A, C.byref(e), C.byref(sh), A, MIS, need, None) == L.MOE_ERR_ALIGN
+    # T = 0 is a no-op (returns before touching the device)
+    s0 = shp(T=0)
+    assert f(C.byref(s0), 0, 0, None, None, 0, 0, 0, None) == L.MOE_OK
+
+
+def test_route_permute_combine_validation(lib):
+    s = shp()
+    need = L.moe_workspace_bytes(s)
+    assert lib.moe_route(C.byref(s), A, 0, A, A, A, need, None) == L.MOE_ERR_NULL
+    assert lib.moe_route(C.byref(s), A, A, MIS, A, A, need, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_route(C.byref(s), A, A, A, A, A, need - 1, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_route_ex(C.byref(s), A, A, A, A, -1.0, A, need, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_route_ex(C.byref(s), A, A, A, A, float("nan"), A, need, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_permute(C.byref(s), 0, A, A, A, A, need, None) == L.MOE_ERR_NULL
+    assert lib.moe_permute(C.byref(s), A, A, MIS, A, A, need, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_permute(C.byref(s), A, A, A, A, None, need, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(C.byref(s), A, 0, A, None, A, None) == L.MOE_ERR_NULL
+    assert lib.moe_combine(C.byref(s), A, A, A, MIS, A, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_combine(C.byref(shp(D=65)), A, A, A, None, A, None) == L.MOE_ERR_SHAPE
+
+
+def test_grouped_gemm_validation(lib):
+    W = L.q4(A, A, A)
+    need = L.moe_grouped_gemm_q4_workspace_bytes(4, 100)
+    g = lambda n_groups=4, rows=100, N=128, K=256, Ap=A, a_rows=100, idx=None, off=A, w=W, ep=0, \
+        Cp=B, ws=A, wsb=need: lib.moe_grouped_gemm_q4(n_groups, rows, N, K, Ap, a_rows, idx, off, w,  # noqa
+                                                     ep, Cp, ws, wsb, None)
+    assert g(n_groups=0) == L.MOE_ERR_SHAPE
+    assert g(N=96) == L.MOE_ERR_SHAPE
+    assert g(K=100) == L.MOE_ERR_SHAPE
+    assert g(ep=2) == L.MOE_ERR_SHAPE
+    assert g(rows=-1) == L.MOE_ERR_SHAPE
+    assert g(rows=1 << 25, N=128) == L.MOE_ERR_SHAPE
+    assert g(rows=0) == L.MOE_OK          # nothing to do, nothing enqueued
+    assert g(Ap=0) == L.MOE_ERR_NULL
+    assert g(off=0) == L.MOE_ERR_NULL
+    assert g(w=L.q4(A, 0, A)) == L.MOE_ERR_NULL
+    assert g(Cp=0) == L.MOE_ERR_NULL
+    assert g(Ap=MIS) == L.MOE_ERR_ALIGN
+    assert g(idx=MIS) == L.MOE_ERR_ALIGN
+    assert g(w=L.q4(A, A, MIS)) == L.MOE_ERR_ALIGN
+    assert g(ws=0) == L.MOE_ERR_WORKSPACE
+    assert g(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.lib()

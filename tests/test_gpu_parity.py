@@ -1,0 +1,388 @@
+"""GPU parity of the HIP path (called through the C ABI) against the fp64 CPU oracle.
+
+Bars: integer work (top-k sets, group offsets, permutation) bit-exact; grouped GEMM on
+exact-integer weights bit-exact after bf16 rounding; bf16 outputs per element within
+|gpu - oracle| <= 2e-2 * RMS(oracle) + 3e-2 * |oracle| (the reading of the stated tolerance,
+derived from the bf16 rounding points of the path).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_grouped_expert_amd import _lib as L
+from bit_grouped_expert_amd import device as dev
+from bit_grouped_expert_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+ATOL_RMS, RTOL = 2e-2, 3e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    L.lib()
+    return torch
+
+
+def bf16f(bits):
+    return oracle.bf16_to_f64(bits)
+
+
+def check_tol(g, o, what):
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(o * o))) if o.size else 0.0
+    err = np.abs(g - o)
+    bound = ATOL_RMS * rms + RTOL * np.abs(o)
+    bad = err > bound
+    say(f"  {what}: max|err|/RMS = {err.max() / rms if rms else 0:.4g}, "
+        f"mean|err|/RMS = {err.mean() / rms if rms else 0:.3g}, "
+        f"failing = {int(bad.sum())}/{err.size}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside tolerance"
+
+
+def sets_equal(idx_gpu, idx_ref):
+    return np.array_equal(np.sort(idx_gpu, axis=1), np.sort(idx_ref, axis=1))
+
+
+# ----------------------------------------------------------------------------- grouped GEMM
+def _q4_codes_words(rng, G, N, K):
+    codes = rng.integers(0, 16, size=(G, N, K), dtype=np.uint8)
+    return codes, wl.pack_codes(codes)
+
+
+GEMM_INT_CASES = [
+    # (counts per group, N, K, gather)
+    ([0, 1, 17, 33, 100], 128, 256, False),
+    ([64, 5, 40], 64, 64, False),            # K = 64: only a trailing half block
+    ([16, 0, 31, 70], 192, 192, True),       # 128 + 64, gathered rows incl. invalid indices
+    ([200, 30], 256, 2048, True),            # 64-row tiles, every fragment count
+    ([3, 0, 0, 9], 512, 512, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GEMM_INT_CASES)))
+def test_grouped_gemm_exact_integer(torch_cuda, case):
+    """scale 1, bias -8, x in {-2..2}: every partial sum is an integer below 2^24, so the
+    bf16-rounded GPU output must equal the bf16 rounding of the exact result bit for bit."""
+    torch = torch_cuda
+    counts, N, K, gather = GEMM_INT_CASES[case]
+    say(f"case {case}: counts={counts} N={N} K={K} gather={gather}")
+    rng = np.random.default_rng(100 + case)
+    G = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(off[-1])
+    codes, words = _q4_codes_words(rng, G, N, K)
+    scale = np.full((G, N, K // 64), 0x3F80, np.uint16)
+    bias = np.full((G, N, K // 64), 0xC100, np.uint16)
+    a_rows = rows + 7
+    xi = rng.integers(-2, 3, size=(a_rows, K))
+    A = wl.f32_to_bf16_bits(xi.astype(np.float32))
+    if gather:
+        ridx = rng.integers(0, a_rows, size=rows).astype(np.int32)
+        ridx[::11] = -1
+        ridx[5::13] = a_rows          # out of range -> zero row
+    else:
+        ridx = None
+    gathered = np.zeros((rows, K))
+    src = ridx if gather else np.arange(rows)
+    ok = (src >= 0) & (src < a_rows)
+    gathered[ok] = bf16f(A[src[ok]])
+    ref = oracle.grouped_gemm_q4(gathered, off, words, scale, bias, 0)
+    want = wl.f32_to_bf16_bits(ref.astype(np.float32))
+    assert np.array_equal(ref, np.round(ref))
+
+    d = dev.to_device
+    Cdev = torch.full((rows, N), 0x7FC1, dtype=torch.int16, device="cuda")
+    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows), dtype=torch.uint8, device="cuda")
+    tw = [d(words), d(scale), d(bias)]
+    keep = [d(A), d(ridx) if gather else None, d(off)]
+    L.moe_grouped_gemm_q4(G, rows, N, K, keep[0], a_rows, keep[1], keep[2], L.q4(*tw), 0, Cdev, ws)
+    torch.cuda.synchronize()
+    got = dev.to_host(Cdev, np.uint16)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} mismatching elements"
+
+
+@pytest.mark.parametrize("epilogue", [0, 1])
+def test_grouped_gemm_float_vs_oracle(torch_cuda, epilogue):
+    torch = torch_cuda
+    rng = np.random.default_rng(7 + epilogue)
+    counts = [0, 3, 16, 29, 64, 90, 1]
+    G, N, K = len(counts), 256, 1024
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(off[-1])
+    cfg = wl.MoEConfig("g", 0, K, G - 1, 1, N // 2)
+    w = wl.make_weights(cfg, 1234 + epilogue)      # gate_up: [G, N, K/8]
+    words, scale, bias = w["gate_up_q"], w["gate_up_s"], w["gate_up_b"]
+    A = wl.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    ref = oracle.grouped_gemm_q4(bf16f(A), off, words, scale, bias, epilogue)
+    d = dev.to_device
+    out_cols = N // 2 if epilogue else N
+    Cdev = torch.zeros((rows, out_cols), dtype=torch.int16, device="cuda")
+    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows), dtype=torch.uint8, device="cuda")
+    tw = [d(words), d(scale), d(bias)]
+    keep = [d(A), d(off)]
+    L.moe_grouped_gemm_q4(G, rows, N, K, keep[0], rows, None, keep[1], L.q4(*tw), epilogue, Cdev, ws)
+    torch.cuda.synchronize()
+    check_tol(bf16f(dev.to_host(Cdev, np.uint16)), ref, f"grouped gemm epilogue={epilogue}")
+
+
+# ----------------------------------------------------------------------------- routing
+ROUTE_CONFIGS = ["tiny", "decode1", "decode4", "prefill512", "zipf8192", "uniform8192", "long32768"]
+
+
+def _route_gpu(torch, cfg, x, router, gap=None):
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    if gap is None:
+        L.moe_route(shp, xd, rd, idx, w, ws)
+    else:
+        L.moe_route_ex(shp, xd, rd, idx, w, gap, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_route(cfg, x, router, gi, gw, exact_order=False):
+    Lref = oracle.router_logits(x, router)
+    ri, rw = oracle.select_topk(Lref, cfg.k)
+    same = np.all(np.sort(gi, 1) == np.sort(ri, 1), axis=1)
+    if not same.all():
+        s = np.sort(Lref, 1)[:, ::-1]
+        bad = np.nonzero(~same)[0]
+        say("  mismatching tokens", bad[:10], "fp64 gaps", (s[bad, cfg.k - 1] - s[bad, cfg.k])[:10])
+    assert same.all(), f"{int((~same).sum())} tokens with a different top-{cfg.k} set"
+    if exact_order:
+        assert np.array_equal(gi, ri)
+    # weights per (token, expert)
+    order_g = np.argsort(gi, 1)
+    order_r = np.argsort(ri, 1)
+    wg = np.take_along_axis(gw, order_g, 1)
+    wr = np.take_along_axis(rw, order_r, 1)
+    assert np.max(np.abs(wg - wr)) < 2e-5, np.max(np.abs(wg - wr))
+    assert np.allclose(gw.sum(1), 1.0, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", ROUTE_CONFIGS)
+def test_route_parity(torch_cuda, name):
+    cfg = wl.CONFIGS[name]
+    say(f"route {name}: T={cfg.T} E={cfg.E} k={cfg.k}")
+    x, router = wl.make_activations(cfg, 0)
+    gi, gw = _route_gpu(torch_cuda, cfg, x, router)
+    _check_route(cfg, x, router, gi, gw)
+
+
+def test_route_forced_refine(torch_cuda):
+    """Every token through the exact fp64 rescoring: the order equals the fp64 order too."""
+    cfg = wl.CONFIGS["prefill512"]
+    x, router = wl.make_activations(cfg, 0)
+    gi, gw = _route_gpu(torch_cuda, cfg, x, router, gap=1e30)
+    _check_route(cfg, x, router, gi, gw, exact_order=True)
+
+
+@pytest.mark.parametrize("E,k,T,D", [(64, 8, 64, 128), (1000, 4, 40, 64), (40, 32, 33, 128)])
+def test_route_exact_ties(torch_cuda, E, k, T, D):
+    """Integer x and router rows (many duplicated) give exactly tied logits: the lower expert id
+    wins and the order is the exact descending order."""
+    rng = np.random.default_rng(E + k)
+    cfg = wl.MoEConfig("ties", T, D, E, k, 64)
+    x = wl.f32_to_bf16_bits(rng.integers(-2, 3, size=(T, D)).astype(np.float32))
+    base = rng.integers(-3, 4, size=(max(E // 4, 2), D)).astype(np.float32)
+    router = base[rng.integers(0, base.shape[0], size=E)]
+    gi, gw = _route_gpu(torch_cuda, cfg, x, router)
+    _check_route(cfg, x, router, gi, gw, exact_order=True)
+
+
+# ----------------------------------------------------------------------------- permutation
+def _permute_gpu(torch, cfg, idx):
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    n = max(cfg.T * cfg.k, 1)
+    off = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+    st = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    sr = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    idx_d = dev.to_device(idx.astype(np.int32))
+    L.moe_permute(shp, idx_d, off, st, sr, ws)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), st.cpu().numpy(), sr.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode1", "prefill512", "zipf8192", "long32768"])
+def test_permute_parity(torch_cuda, name):
+    cfg = wl.CONFIGS[name]
+    say(f"permute {name}")
+    x, router = wl.make_activations(cfg, 0)
+    idx, _ = oracle.select_topk(oracle.router_logits(x, router), cfg.k)
+    off, st, sr = _permute_gpu(torch_cuda, cfg, idx)
+    r_off, r_st, r_sr = oracle.stable_permutation(idx, cfg.E)
+    assert np.array_equal(off, r_off)
+    assert np.array_equal(st, r_st)
+    assert np.array_equal(sr, r_sr)
+
+
+def test_permute_invalid_entries_and_empty(torch_cuda):
+    """Entries outside [0, E) are ignored: they behave like an extra expert after the last
+    one that is then dropped, and their slot_row is -1."""
+    cfg = wl.MoEConfig("inv", 700, 64, 30, 3, 64)
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.permutation(cfg.E)[:cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    idx[::17, 1] = -1
+    idx[5::23, 2] = cfg.E
+    off, st, sr = _permute_gpu(torch_cuda, cfg, idx)
+    mapped = np.where((idx < 0) | (idx >= cfg.E), cfg.E, idx)
+    r_off, r_st, r_sr = oracle.stable_permutation(mapped, cfg.E + 1)
+    valid = (idx.ravel() >= 0) & (idx.ravel() < cfg.E)
+    assert np.array_equal(off, r_off[:cfg.E + 1])
+    n = r_off[cfg.E]
+    assert np.array_equal(st[:n], r_st[:n])
+    assert np.array_equal(sr[valid], r_sr[valid])
+    assert np.all(sr[~valid] == -1)
+    # T = 0: offsets all zero
+    cfg0 = wl.MoEConfig("empty", 0, 64, 30, 3, 64)
+    off0, _, _ = _permute_gpu(torch_cuda, cfg0, np.zeros((0, 3), np.int32))
+    assert np.all(off0 == 0)
+
+
+# ----------------------------------------------------------------------------- combine
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_combine_parity(torch_cuda, with_shared):
+    torch = torch_cuda
+    cfg = wl.MoEConfig("c", 300, 2048 + 64, 32, 5, 64)
+    T, D, k = cfg.T, cfg.D, cfg.k
+    rng = np.random.default_rng(9)
+    Y = wl.f32_to_bf16_bits(rng.standard_normal((T * k, D)).astype(np.float32))
+    S = wl.f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    sr = rng.permutation(T * k).astype(np.int32)
+    sr[::19] = -1
+    sr[7::31] = T * k
+    out = torch.empty((T, D), dtype=torch.int16, device="cuda")
+    keep = [dev.to_device(Y), dev.to_device(sr), dev.to_device(w), dev.to_device(S)]
+    L.moe_combine(L.shape(T, D, cfg.E, k, cfg.F), keep[0], keep[1], keep[2],
+                  keep[3] if with_shared else None, out)
+    torch.cuda.synchronize()
+    valid = (sr >= 0) & (sr < T * k)
+    w_eff = np.where(valid.reshape(T, k), w, 0.0)
+    ref = oracle.combine(bf16f(Y), np.where(valid, sr, 0), w_eff,
+                         bf16f(S) if with_shared else np.zeros((T, D)))
+    check_tol(bf16f(dev.to_host(out, np.uint16)), ref, "combine")
+
+
+# ----------------------------------------------------------------------------- whole layer
+def _layer_gpu(torch, cfg, x, router, lw, with_shared=True):
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    L.moe_layer_forward(shp, xd, rd, lw.experts, lw.shared if with_shared else None, out, ws)
+    torch.cuda.synchronize()
+    lay = L.moe_workspace_layout(shp)
+    wsn = ws.cpu().numpy()
+
+    def grab(off, count, dtype):
+        return wsn[off:off + count * np.dtype(dtype).itemsize].view(dtype)
+    inter = {
+        "idx": grab(lay.topk_idx, cfg.T * cfg.k, np.int32).reshape(cfg.T, cfg.k),
+        "w": grab(lay.topk_w, cfg.T * cfg.k, np.float32).reshape(cfg.T, cfg.k),
+        "offsets": grab(lay.offsets, cfg.E + 2, np.int32),
+        "sorted_tok": grab(lay.sorted_tok, (cfg.k + 1) * cfg.T, np.int32),
+        "slot_row": grab(lay.slot_row, cfg.T * cfg.k, np.int32),
+    }
+    return dev.to_host(out, np.uint16), inter
+
+
+def _check_layer_integer_stages(cfg, x, router, inter, with_shared=True):
+    idx = inter["idx"]
+    ri, _ = oracle.select_topk(oracle.router_logits(x, router), cfg.k)
+    assert sets_equal(idx, ri), "top-k sets differ"
+    r_off, r_st, r_sr = oracle.stable_permutation(idx, cfg.E)
+    assert np.array_equal(inter["offsets"][:cfg.E + 1], r_off)
+    n = cfg.T * cfg.k
+    assert np.array_equal(inter["sorted_tok"][:n], r_st)
+    assert np.array_equal(inter["slot_row"], r_sr)
+    if with_shared:
+        assert inter["offsets"][cfg.E + 1] == n + cfg.T
+        assert np.array_equal(inter["sorted_tok"][n:], np.arange(cfg.T))
+
+
+FULL_LAYER = ["tiny", "decode1", "decode4", "prefill512"]
+
+
+@pytest.mark.parametrize("name", FULL_LAYER)
+def test_layer_forward_parity_full(torch_cuda, name):
+    cfg = wl.CONFIGS[name]
+    say(f"layer {name}: full oracle")
+    x, router = wl.make_activations(cfg, 0)
+    w = wl.make_weights(cfg, wl.layer_seed(0))
+    lw = dev.LayerWeights(w, cfg.E)
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw)
+    _check_layer_integer_stages(cfg, x, router, inter)
+    ref = oracle.moe_layer(x, router, w, cfg.k)
+    check_tol(bf16f(got), ref["out"], f"layer {name} out")
+
+
+@pytest.mark.parametrize("name,n_tok", [("zipf8192", 96), ("uniform8192", 64), ("long32768", 24)])
+def test_layer_forward_parity_sampled(torch_cuda, name, n_tok):
+    """Full-size layers: integer stages checked on every token, outputs on a seeded sample of
+    tokens (first, last and random) evaluated one by one by the oracle.  The long-prompt chunk
+    runs its four distinct weight sets back to back on the same x."""
+    cfg = wl.CONFIGS[name]
+    x, router = wl.make_activations(cfg, 0)
+    rng = np.random.default_rng(2024)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, n_tok - 2)]))
+    for layer in range(cfg.n_layers):
+        say(f"layer {name} #{layer}: {len(toks)} sampled tokens")
+        w = wl.make_weights(cfg, wl.layer_seed(layer))
+        lw = dev.LayerWeights(w, cfg.E)
+        got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw)
+        del lw
+        _check_layer_integer_stages(cfg, x, router, inter)
+        ref, _, _ = oracle.moe_out_for_tokens(x, router, w, cfg.k, toks)
+        check_tol(bf16f(got[toks]), ref, f"layer {name} #{layer} sampled out")
+
+
+def test_layer_forward_no_shared(torch_cuda):
+    cfg = wl.CONFIGS["tiny"]
+    x, router = wl.make_activations(cfg, 0)
+    w = wl.make_weights(cfg, 1000)
+    lw = dev.LayerWeights(w, cfg.E)
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw, with_shared=False)
+    _check_layer_integer_stages(cfg, x, router, inter, with_shared=False)
+    ref = oracle.moe_layer(x, router, w, cfg.k, with_shared=False)
+    check_tol(bf16f(got), ref["out"], "tiny without shared expert")
+
+
+@pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192)])
+def test_layer_forward_odd_shapes(torch_cuda, shape):
+    """Wide top-k (k = 32), many experts (E = 1000), K % 128 == 64 (D = F = 192), a single expert
+    per token."""
+    T, D, E, k, F = shape
+    cfg = wl.MoEConfig("odd", T, D, E, k, F)
+    x, router = wl.make_activations(cfg, 5)
+    w = wl.make_weights(cfg, 77)
+    lw = dev.LayerWeights(w, cfg.E)
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw)
+    _check_layer_integer_stages(cfg, x, router, inter)
+    ref = oracle.moe_layer(x, router, w, cfg.k)
+    check_tol(bf16f(got), ref["out"], f"layer {shape}")
+
+
+def test_layer_forward_deterministic(torch_cuda):
+    cfg = wl.CONFIGS["prefill512"]
+    x, router = wl.make_activations(cfg, 0)
+    lw = dev.LayerWeights(wl.make_weights(cfg, 1000), cfg.E)
+    a, _ = _layer_gpu(torch_cuda, cfg, x, router, lw)
+    b, _ = _layer_gpu(torch_cuda, cfg, x, router, lw)
+    assert np.array_equal(a, b)
