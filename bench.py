@@ -143,6 +143,10 @@ def main():
     # ---- per-stage durations: HIP events recorded by the library on the same stream
     nst = L.N_STAGE_EVENTS
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
+    for row in evs:          # torch creates the HIP event on its first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
     for i in range(args.steps):
         lw = sets[i % len(sets)]
         L.moe_layer_forward_events(shp, xd, rd, lw.experts, lw.shared, out, ws, evs[i],

@@ -176,13 +176,16 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
                        hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!topk_idx || !offsets || !sorted_tok || !slot_row) return MOE_ERR_NULL;
-  if (!aligned16(topk_idx) || !aligned16(offsets) || !aligned16(sorted_tok) || !aligned16(slot_row))
+  // with T == 0 only the offsets are written; the empty arrays may be NULL
+  const bool empty = shape->T == 0;
+  if (!offsets || (!empty && (!topk_idx || !sorted_tok || !slot_row))) return MOE_ERR_NULL;
+  if (!aligned16(offsets) ||
+      (!empty && (!aligned16(topk_idx) || !aligned16(sorted_tok) || !aligned16(slot_row))))
     return MOE_ERR_ALIGN;
   const Layout L = make_layout(shape);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
-  if (shape->T == 0) {
+  if (empty) {
     // empty routing still defines offsets (all zero): a scan over zero chunks
     launch_scan(at<int32_t>(ws, L.chunk_cnt), 0, shape->n_experts, offsets, -1, stream);
     return launch_status();

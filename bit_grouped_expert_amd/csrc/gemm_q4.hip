@@ -205,11 +205,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int g, int row0, 
             }
           }
         }
-        const float s0 = grp ? bf16hi_to_f32(sw0) : bf16lo_to_f32(sw0);
-        const float s1 = grp ? bf16hi_to_f32(sw1) : bf16lo_to_f32(sw1);
-        const float bp0 = fmaf(-128.f, s0, grp ? bf16hi_to_f32(bw0) : bf16lo_to_f32(bw0));
-        const float bp1 = fmaf(-128.f, s1, grp ? bf16hi_to_f32(bw1) : bf16lo_to_f32(bw1));
-        const int gl = (kb >> 6) + grp;
+        // scale group of these two steps (words 0..7 -> first, 8..15 -> second), read off
+        // the tracked word index so it never depends on the swap's direction
+        const int gsel = __builtin_amdgcn_readfirstlane((int)(widx[2 * grp] >> 3));
+        const float s0 = gsel ? bf16hi_to_f32(sw0) : bf16lo_to_f32(sw0);
+        const float s1 = gsel ? bf16hi_to_f32(sw1) : bf16lo_to_f32(sw1);
+        const float bp0 = fmaf(-128.f, s0, gsel ? bf16hi_to_f32(bw0) : bf16lo_to_f32(bw0));
+        const float bp1 = fmaf(-128.f, s1, gsel ? bf16hi_to_f32(bw1) : bf16lo_to_f32(bw1));
+        const int gl = (kb >> 6) + gsel;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const f32x4_t X = *(const f32x4_t*)(Xs + gl * NR + f * 16 + 4 * q);

@@ -137,7 +137,8 @@ moe_status moe_route_ex(const moe_shape* shape, const uint16_t* x, const float* 
  *   offsets    int32 [E + 1]: rows of expert e are offsets[e]..offsets[e+1]-1
  *   sorted_tok int32 [T*k]: token of each permuted row, ascending within a group
  *   slot_row   int32 [T*k]: slot_row[t*k + j] = permuted row of pair (t, j)
- *   ws         >= moe_workspace_bytes(shape) bytes. */
+ *   ws         >= moe_workspace_bytes(shape) bytes.
+ * With T == 0 only `offsets` (all zero) is written and the other arrays may be NULL. */
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
                        int32_t* sorted_tok, int32_t* slot_row, void* ws, size_t ws_bytes,
                        hipStream_t stream);

@@ -112,6 +112,9 @@ def test_route_permute_combine_validation(lib):
     assert lib.moe_permute(C.byref(s), 0, A, A, A, A, need, None) == L.MOE_ERR_NULL
     assert lib.moe_permute(C.byref(s), A, A, MIS, A, A, need, None) == L.MOE_ERR_ALIGN
     assert lib.moe_permute(C.byref(s), A, A, A, A, None, need, None) == L.MOE_ERR_WORKSPACE
+    s0 = shp(T=0)       # empty routing: only the offsets are required
+    assert lib.moe_permute(C.byref(s0), None, None, None, None, A, need, None) == L.MOE_ERR_NULL
+    assert lib.moe_permute(C.byref(s0), None, MIS, None, None, A, need, None) == L.MOE_ERR_ALIGN
     assert lib.moe_combine(C.byref(s), A, 0, A, None, A, None) == L.MOE_ERR_NULL
     assert lib.moe_combine(C.byref(s), A, A, A, MIS, A, None) == L.MOE_ERR_ALIGN
     assert lib.moe_combine(C.byref(shp(D=65)), A, A, A, None, A, None) == L.MOE_ERR_SHAPE
