@@ -49,7 +49,8 @@ _SIGS = {
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_workspace_bytes": (C.c_size_t, [C.POINTER(moe_shape)]),
     "moe_workspace_layout": (C.c_int, [C.POINTER(moe_shape), C.POINTER(moe_ws_layout)]),
-    "moe_grouped_gemm_q4_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
+    "moe_grouped_gemm_q4_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32,
+                                                         C.c_int32]),
     "moe_route": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                             C.c_void_p, C.c_size_t, C.c_void_p]),
     "moe_route_ex": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p, C.c_void_p,
@@ -137,8 +138,8 @@ def moe_workspace_layout(shp: moe_shape) -> moe_ws_layout:
     return out
 
 
-def moe_grouped_gemm_q4_workspace_bytes(n_groups: int, rows_total: int) -> int:
-    return lib().moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total)
+def moe_grouped_gemm_q4_workspace_bytes(n_groups: int, rows_total: int, a_rows: int, K: int) -> int:
+    return lib().moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total, a_rows, K)
 
 
 def moe_route(shp, x, router_w, topk_idx, topk_w, ws, ws_bytes=None, stream=None):

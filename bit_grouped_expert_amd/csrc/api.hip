@@ -1,6 +1,7 @@
 // C ABI of libmoeq4: host-side validation, workspace carving and launches.
 // Every entry point validates on the host before it enqueues anything, then
 // enqueues its kernels on the caller's stream and returns without waiting.
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/moeq4.h"
@@ -29,16 +30,42 @@ moe_status check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
-// rows per tile of the grouped GEMMs inside the layer: 32 while groups average
-// at most 64 rows, 64 beyond
-int layer_bm(const moe_shape* s) {
-  const int64_t rows = (int64_t)(s->top_k + 1) * s->T;
-  return rows <= 64 * (int64_t)(s->n_experts + 1) ? 32 : 64;
+// Which grouped-GEMM engine runs, and its tile rows.  The grouped engine (tiles of
+// up to 64 rows, persistent XCD-aware grid, exact affine arithmetic) serves every
+// group size.  The environment variable MOEQ4_GEMM=rows selects the first
+// register-streaming engine instead (tiles of 32 or 64 rows, one workgroup per
+// tile and slice), kept for comparison; anything else selects the grouped engine.
+struct GemmPlan {
+  bool grouped;
+  int bm;
+};
+
+GemmPlan plan_gemm(int64_t rows, int n_groups) {
+  const int64_t g = n_groups > 0 ? n_groups : 1;
+  const char* env = getenv("MOEQ4_GEMM");
+  if (env && strcmp(env, "rows") == 0) return GemmPlan{false, rows <= 64 * g ? 32 : 64};
+  return GemmPlan{true, kGroupedBM};
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Grouped GEMM launch with the plan's engine (the tile map is already built with plan.bm).
+void run_gemm(GemmParams p, const GemmPlan& plan, bool swiglu, int64_t rows, int n_groups,
+              hipStream_t stream) {
+  const int64_t bound = max_tiles(rows, n_groups, plan.bm);
+  if (plan.grouped) launch_grouped(p, swiglu, bound, device_cu_count(), stream);
+  else launch_gemm_q4(p, plan.bm, swiglu, bound, stream);
 }
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, act, y, total;
+      tile_count, xsum_x, xsum_act, act, y, total;
 };
 
 Layout make_layout(const moe_shape* s) {
@@ -61,6 +88,8 @@ Layout make_layout(const moe_shape* s) {
   L.slot_row = take(T * k * 4);
   L.tiles = take((size_t)max_tiles(rows_ext, (int)E + 1, 32) * sizeof(int4));
   L.tile_count = take(16);
+  L.xsum_x = take(T * (D / 64) * 4);
+  L.xsum_act = take(rows_ext * (F / 64) * 4);
   L.act = take(rows_ext * F * 2);
   L.y = take(rows_ext * D * 2);
   L.total = o;
@@ -120,9 +149,24 @@ moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout) {
   return MOE_OK;
 }
 
-size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total) {
-  if (n_groups < 1 || rows_total < 0) return 0;
-  return align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4)) + kAlign;
+namespace {
+struct GemmWs {
+  size_t tiles, tile_count, xsum, total;
+};
+GemmWs gemm_ws(int32_t n_groups, int32_t rows_total, int32_t a_rows, int32_t K) {
+  GemmWs w;
+  w.tiles = 0;
+  w.tile_count = align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4));
+  w.xsum = w.tile_count + kAlign;
+  w.total = w.xsum + align_up((size_t)a_rows * (size_t)(K / 64) * 4);
+  return w;
+}
+}  // namespace
+
+size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total, int32_t a_rows,
+                                           int32_t K) {
+  if (n_groups < 1 || rows_total < 0 || a_rows < 0 || K <= 0 || K % 64) return 0;
+  return gemm_ws(n_groups, rows_total, a_rows, K).total;
 }
 
 static moe_status route_impl(const moe_shape* shape, const uint16_t* x, const float* router_w,
@@ -211,16 +255,16 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
   if (!aligned16(A) || !aligned16(offsets) || !q4_aligned(W) || !aligned16(C) ||
       (a_row_index && !aligned16(a_row_index)))
     return MOE_ERR_ALIGN;
-  const size_t need = moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const GemmWs gw = gemm_ws(n_groups, rows_total, a_rows, K);
+  if (!ws || ws_bytes < gw.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
 
-  const int bm = rows_total <= 64 * (int64_t)n_groups ? 32 : 64;
-  const int64_t bound = max_tiles(rows_total, n_groups, bm);
-  int4* tiles = at<int4>(ws, 0);
-  int32_t* tile_count =
-      at<int32_t>(ws, align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4)));
-  launch_build_tiles(offsets, n_groups, rows_total, bm, tiles, tile_count, stream);
+  const GemmPlan plan = plan_gemm(rows_total, n_groups);
+  int4* tiles = at<int4>(ws, gw.tiles);
+  int32_t* tile_count = at<int32_t>(ws, gw.tile_count);
+  float* xsum = at<float>(ws, gw.xsum);
+  if (plan.grouped) launch_row_group_sums(A, a_rows, K, xsum, stream);
+  launch_build_tiles(offsets, n_groups, rows_total, plan.bm, tiles, tile_count, stream);
 
   GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -236,7 +280,9 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
   p.ldc = epilogue == 1 ? N / 2 : N;
   p.tiles = tiles;
   p.tile_count = tile_count;
-  launch_gemm_q4(p, bm, epilogue == 1, bound, stream);
+  p.xsum = xsum;
+  p.xsum_ld = K / 64;
+  run_gemm(p, plan, epilogue == 1, rows_total, n_groups, stream);
   return launch_status();
 }
 
@@ -287,6 +333,8 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
   uint16_t* act = at<uint16_t>(ws, L.act);
   uint16_t* y = at<uint16_t>(ws, L.y);
+  float* xsum_x = at<float>(ws, L.xsum_x);
+  float* xsum_act = at<float>(ws, L.xsum_act);
 
   auto mark = [&](int i) {
     if (events && events[i]) hipEventRecord(events[i], stream);
@@ -302,9 +350,9 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
   permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
                has_shared ? T : -1, stream);
-  const int bm = layer_bm(shape);
-  const int64_t bound = max_tiles(rows, n_groups, bm);
-  launch_build_tiles(offsets, n_groups, rows, bm, tiles, tile_count, stream);
+  const GemmPlan plan = plan_gemm(rows, n_groups);
+  launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
+  if (plan.grouped) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
 
   // gate_up + SwiGLU: x rows gathered through sorted_tok -> act [rows, F]
@@ -323,7 +371,11 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   p.ldc = F;
   p.tiles = tiles;
   p.tile_count = tile_count;
-  launch_gemm_q4(p, bm, true, bound, stream);
+  p.xsum = xsum_x;          // gathered through sorted_tok like the rows of x
+  p.xsum_ld = D / 64;
+  p.xsum_out = xsum_act;    // row sums of act for the down GEMM
+  p.xsum_out_ld = F / 64;
+  run_gemm(p, plan, true, rows, n_groups, stream);
   mark(3);
 
   // down: act rows in order -> y [rows, D]
@@ -336,7 +388,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   p.K = F;
   p.C = y;
   p.ldc = D;
-  launch_gemm_q4(p, bm, false, bound, stream);
+  p.xsum = xsum_act;
+  p.xsum_ld = F / 64;
+  p.xsum_out = nullptr;
+  run_gemm(p, plan, false, rows, n_groups, stream);
   mark(4);
 
   // combine with the shared expert (rows T*k.. of y)

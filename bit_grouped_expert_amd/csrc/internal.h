@@ -44,6 +44,10 @@ struct GemmParams {
   const int4* tiles;          // (group, row0, rows, 0)
   const int32_t* tile_count;
   int32_t n_slices;
+  const float* xsum;          // [a_rows, xsum_ld] row sums of A per 64-wide K group
+  int32_t xsum_ld;
+  float* xsum_out;            // nullable; SwiGLU only: row sums of C per 64 columns
+  int32_t xsum_out_ld;
 };
 
 inline int64_t max_tiles(int64_t rows_total, int n_groups, int bm) {
@@ -54,6 +58,16 @@ void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, in
 // bm: 32 or 64 rows per tile.  Grid = max_tiles(rows_total, n_groups, bm) * n_slices.
 void launch_gemm_q4(GemmParams p, int bm, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
 int gemm_q4_slices(int N, bool swiglu);
+
+// Grouped engine for every group size: tiles of up to 32 rows (tile map built with
+// bm = 32), persistent XCD-aware grid of about 2 workgroups per compute unit.  Needs
+// p.xsum (row sums of A per 64-wide group); with SwiGLU it can also write the row sums
+// of its output (p.xsum_out) for the next GEMM.
+constexpr int kGroupedBM = 32;
+void launch_grouped(GemmParams p, bool swiglu, int64_t n_tiles_bound, int n_cu, hipStream_t s);
+int grouped_slices(int N, bool swiglu);
+// out[r][g] = sum of A[r][64g .. 64g+63] in fp32, A bf16 [rows, K]
+void launch_row_group_sums(const uint16_t* A, int rows, int K, float* out, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,

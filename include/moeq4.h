@@ -104,8 +104,10 @@ size_t moe_workspace_bytes(const moe_shape* shape);
 /* Fills `layout` for `shape`.  Host-only. */
 moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout);
 
-/* Workspace bytes moe_grouped_gemm_q4 needs (its tile map).  Host-only, pure. */
-size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total);
+/* Workspace bytes moe_grouped_gemm_q4 needs (its tile map and the per-64 row sums
+ * of A).  Host-only, pure; 0 if the arguments are invalid. */
+size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total, int32_t a_rows,
+                                           int32_t K);
 
 /* Router: L = x R^T in fp32 (bf16 x split-exact against a three-way bf16 split
  * of R), top-k by descending logit with exact ties to the lower expert id;
@@ -156,7 +158,12 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
  *              values are clamped to [0, rows_total]; C rows outside every
  *              group are not written
  *   W          q [n_groups, N, K/8], scale/bias [n_groups, N, K/64]
- *   ws         >= moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total). */
+ *   ws         >= moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total, a_rows, K).
+ * Arithmetic: no weight is rounded; each 64-wide group's partial sum is formed on
+ * the matrix cores from the exact values 128 + q and scaled in fp32, so H is the
+ * fp32-accumulated product with the exactly dequantized weights.  The environment
+ * variable MOEQ4_GEMM=rows selects an older engine with the same arithmetic (kept
+ * for comparison). */
 moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
                                const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
                                const int32_t* offsets, moe_q4 W, int32_t epilogue,

@@ -72,8 +72,12 @@ def test_workspace_bytes_monotone_and_layout(lib):
         assert all(o % 256 == 0 for o in offs)
         assert offs == sorted(offs) and lay.total == n
         assert lay.y + (9 * T) * 2048 * 2 <= n
-    assert L.moe_grouped_gemm_q4_workspace_bytes(0, 10) == 0
-    assert L.moe_grouped_gemm_q4_workspace_bytes(257, 4608) >= (4608 // 32 + 257) * 16
+    assert L.moe_grouped_gemm_q4_workspace_bytes(0, 10, 10, 64) == 0
+    assert L.moe_grouped_gemm_q4_workspace_bytes(4, 10, 10, 96) == 0       # K % 64 != 0
+    assert L.moe_grouped_gemm_q4_workspace_bytes(4, 10, -1, 64) == 0
+    need = L.moe_grouped_gemm_q4_workspace_bytes(257, 4608, 512, 2048)
+    assert need >= (4608 // 32 + 257) * 16 + 512 * 32 * 4       # tile map + row sums of A
+    assert L.moe_grouped_gemm_q4_workspace_bytes(257, 4608, 1024, 2048) > need
 
 
 def ffn(q=A, s=A, b=A):
@@ -122,7 +126,7 @@ def test_route_permute_combine_validation(lib):
 
 def test_grouped_gemm_validation(lib):
     W = L.q4(A, A, A)
-    need = L.moe_grouped_gemm_q4_workspace_bytes(4, 100)
+    need = L.moe_grouped_gemm_q4_workspace_bytes(4, 100, 100, 256)
     g = lambda n_groups=4, rows=100, N=128, K=256, Ap=A, a_rows=100, idx=None, off=A, w=W, ep=0, \
         Cp=B, ws=A, wsb=need: lib.moe_grouped_gemm_q4(n_groups, rows, N, K, Ap, a_rows, idx, off, w,  # noqa
                                                      ep, Cp, ws, wsb, None)

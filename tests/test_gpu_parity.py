@@ -6,6 +6,7 @@ exact-integer weights bit-exact after bf16 rounding; bf16 outputs per element wi
 derived from the bf16 rounding points of the path).
 """
 import math
+import os
 import sys
 
 import numpy as np
@@ -32,6 +33,21 @@ def torch_cuda():
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     L.lib()
     return torch
+
+
+ENGINES = ["rows", "grouped"]
+
+
+@pytest.fixture
+def engine(request):
+    """Force one grouped-GEMM engine (MOEQ4_GEMM) for the duration of a test."""
+    old = os.environ.get("MOEQ4_GEMM")
+    os.environ["MOEQ4_GEMM"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("MOEQ4_GEMM", None)
+    else:
+        os.environ["MOEQ4_GEMM"] = old
 
 
 def bf16f(bits):
@@ -68,23 +84,27 @@ GEMM_INT_CASES = [
     ([16, 0, 31, 70], 192, 192, True),       # 128 + 64, gathered rows incl. invalid indices
     ([200, 30], 256, 2048, True),            # 64-row tiles, every fragment count
     ([3, 0, 0, 9], 512, 512, False),
+    ([127, 128, 129, 0, 300, 1], 384, 320, True),   # 128-row tiles: full, ragged, partial waves
 ]
 
 
+@pytest.mark.parametrize("engine", ENGINES, indirect=True)
+@pytest.mark.parametrize("bias_val", [-8, -5])
 @pytest.mark.parametrize("case", range(len(GEMM_INT_CASES)))
-def test_grouped_gemm_exact_integer(torch_cuda, case):
-    """scale 1, bias -8, x in {-2..2}: every partial sum is an integer below 2^24, so the
-    bf16-rounded GPU output must equal the bf16 rounding of the exact result bit for bit."""
+def test_grouped_gemm_exact_integer(torch_cuda, case, bias_val, engine):
+    """scale 1, bias -8 or -5 (w = q - 8 or q - 5), x in {-2..2}: every partial sum is an
+    integer below 2^24, so the bf16-rounded GPU output must equal the bf16 rounding of the
+    exact result bit for bit.  Bias -5 exercises the path for b != -8 s."""
     torch = torch_cuda
     counts, N, K, gather = GEMM_INT_CASES[case]
-    say(f"case {case}: counts={counts} N={N} K={K} gather={gather}")
+    say(f"case {case} [{engine}] bias {bias_val}: counts={counts} N={N} K={K} gather={gather}")
     rng = np.random.default_rng(100 + case)
     G = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(off[-1])
     codes, words = _q4_codes_words(rng, G, N, K)
     scale = np.full((G, N, K // 64), 0x3F80, np.uint16)
-    bias = np.full((G, N, K // 64), 0xC100, np.uint16)
+    bias = np.full((G, N, K // 64), wl.f32_to_bf16_bits(np.float32(bias_val)), np.uint16)
     a_rows = rows + 7
     xi = rng.integers(-2, 3, size=(a_rows, K))
     A = wl.f32_to_bf16_bits(xi.astype(np.float32))
@@ -104,7 +124,8 @@ def test_grouped_gemm_exact_integer(torch_cuda, case):
 
     d = dev.to_device
     Cdev = torch.full((rows, N), 0x7FC1, dtype=torch.int16, device="cuda")
-    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows, a_rows, K), dtype=torch.uint8,
+                     device="cuda")
     tw = [d(words), d(scale), d(bias)]
     keep = [d(A), d(ridx) if gather else None, d(off)]
     L.moe_grouped_gemm_q4(G, rows, N, K, keep[0], a_rows, keep[1], keep[2], L.q4(*tw), 0, Cdev, ws)
@@ -113,23 +134,31 @@ def test_grouped_gemm_exact_integer(torch_cuda, case):
     assert np.array_equal(got, want), f"{int((got != want).sum())} mismatching elements"
 
 
+@pytest.mark.parametrize("engine", ENGINES, indirect=True)
+@pytest.mark.parametrize("free_bias", [False, True])
 @pytest.mark.parametrize("epilogue", [0, 1])
-def test_grouped_gemm_float_vs_oracle(torch_cuda, epilogue):
+@pytest.mark.parametrize("counts", [[0, 3, 16, 29, 64, 90, 1], [250, 0, 131, 7, 384]])
+def test_grouped_gemm_float_vs_oracle(torch_cuda, epilogue, counts, free_bias, engine):
+    """Float weights: the generator's (bias = -8 scale) and, with free_bias, general affine
+    weights whose bias is drawn independently of the scale."""
     torch = torch_cuda
     rng = np.random.default_rng(7 + epilogue)
-    counts = [0, 3, 16, 29, 64, 90, 1]
+    say(f"float gemm [{engine}] epilogue={epilogue} counts={counts} free_bias={free_bias}")
     G, N, K = len(counts), 256, 1024
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(off[-1])
     cfg = wl.MoEConfig("g", 0, K, G - 1, 1, N // 2)
     w = wl.make_weights(cfg, 1234 + epilogue)      # gate_up: [G, N, K/8]
     words, scale, bias = w["gate_up_q"], w["gate_up_s"], w["gate_up_b"]
+    if free_bias:
+        bias = wl.f32_to_bf16_bits(rng.standard_normal(bias.shape).astype(np.float32) * 0.1)
     A = wl.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
     ref = oracle.grouped_gemm_q4(bf16f(A), off, words, scale, bias, epilogue)
     d = dev.to_device
     out_cols = N // 2 if epilogue else N
     Cdev = torch.zeros((rows, out_cols), dtype=torch.int16, device="cuda")
-    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows, rows, K), dtype=torch.uint8,
+                     device="cuda")
     tw = [d(words), d(scale), d(bias)]
     keep = [d(A), d(off)]
     L.moe_grouped_gemm_q4(G, rows, N, K, keep[0], rows, None, keep[1], L.q4(*tw), epilogue, Cdev, ws)
@@ -324,13 +353,26 @@ FULL_LAYER = ["tiny", "decode1", "decode4", "prefill512"]
 def test_layer_forward_parity_full(torch_cuda, name):
     cfg = wl.CONFIGS[name]
     say(f"layer {name}: full oracle")
+    _layer_full_check(torch_cuda, cfg)
+
+
+@pytest.mark.parametrize("engine", ["rows"], indirect=True)
+@pytest.mark.parametrize("name", ["tiny", "prefill512"])
+def test_layer_forward_parity_full_rows(torch_cuda, name, engine):
+    """The same layers through the older register-streaming engine."""
+    cfg = wl.CONFIGS[name]
+    say(f"layer {name} [{engine}]: full oracle")
+    _layer_full_check(torch_cuda, cfg)
+
+
+def _layer_full_check(torch_cuda, cfg):
     x, router = wl.make_activations(cfg, 0)
     w = wl.make_weights(cfg, wl.layer_seed(0))
     lw = dev.LayerWeights(w, cfg.E)
     got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw)
     _check_layer_integer_stages(cfg, x, router, inter)
     ref = oracle.moe_layer(x, router, w, cfg.k)
-    check_tol(bf16f(got), ref["out"], f"layer {name} out")
+    check_tol(bf16f(got), ref["out"], f"layer {cfg.name} out")
 
 
 @pytest.mark.parametrize("name,n_tok", [("zipf8192", 96), ("uniform8192", 64), ("long32768", 24)])
@@ -364,8 +406,10 @@ def test_layer_forward_no_shared(torch_cuda):
     check_tol(bf16f(got), ref["out"], "tiny without shared expert")
 
 
-@pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192)])
-def test_layer_forward_odd_shapes(torch_cuda, shape):
+@pytest.mark.parametrize("engine", ENGINES, indirect=True)
+@pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192),
+                                   (1500, 320, 4, 2, 192)])
+def test_layer_forward_odd_shapes(torch_cuda, shape, engine):
     """Wide top-k (k = 32), many experts (E = 1000), K % 128 == 64 (D = F = 192), a single expert
     per token."""
     T, D, E, k, F = shape
