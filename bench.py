@@ -176,17 +176,19 @@ def main():
         roof["traffic"] = t["fetch_kib"] * 1024 * scale_f + t["write_kib"] * 1024 * scale_w
     else:
         roof["traffic"] = None
-    roof["kernel"] = "q4_gemm_rows_kernel (grouped gate_up + SwiGLU)"
+    roof["kernel"] = "grouped gate_up + SwiGLU (q4_grouped_kernel)"
     roof["algorithmic_bytes"] = gb
     roof["algorithmic_flops"] = gf
     roof["kernel_us"] = gu_s * 1e6
 
     if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # a plain elementwise copy of 1 GiB (torch's vectorized elementwise kernel): the
+        # reference for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
-        log("bench: copy probe (1 GiB) done")
+        log("bench: copy probe (1 GiB elementwise) done")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -30,21 +30,28 @@ moe_status check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
-// Which grouped-GEMM engine runs, and its tile rows.  The grouped engine (tiles of
-// up to 64 rows, persistent XCD-aware grid, exact affine arithmetic) serves every
-// group size.  The environment variable MOEQ4_GEMM=rows selects the first
-// register-streaming engine instead (tiles of 32 or 64 rows, one workgroup per
-// tile and slice), kept for comparison; anything else selects the grouped engine.
+// Which grouped-GEMM engine runs, and its tile rows.
+//   grouped (default): register-prefetched grouped engine, tiles of 32 rows;
+//   stream  (needs K % 128 == 0): operands streamed through an LDS ring by direct
+//           global->LDS loads; tiles of 32 rows, or 64 when groups average at
+//           least 48 rows;
+//   rows:   the first register-streaming engine, one workgroup per tile and slice.
+// The environment variable MOEQ4_GEMM=stream|grouped|rows forces one (for
+// measurement and tests; stream falls back to grouped where it does not apply).
+enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM };
 struct GemmPlan {
-  bool grouped;
+  Engine eng;
   int bm;
 };
 
-GemmPlan plan_gemm(int64_t rows, int n_groups) {
+GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok) {
   const int64_t g = n_groups > 0 ? n_groups : 1;
   const char* env = getenv("MOEQ4_GEMM");
-  if (env && strcmp(env, "rows") == 0) return GemmPlan{false, rows <= 64 * g ? 32 : 64};
-  return GemmPlan{true, kGroupedBM};
+  if (env && strcmp(env, "rows") == 0) return GemmPlan{ENG_ROWS, rows <= 64 * g ? 32 : 64};
+  if (env && strcmp(env, "grouped") == 0) return GemmPlan{ENG_GROUPED, kGroupedBM};
+  if (env && strcmp(env, "stream") == 0 && stream_ok)
+    return GemmPlan{ENG_STREAM, rows >= 48 * g ? 64 : 32};
+  return GemmPlan{ENG_GROUPED, kGroupedBM};
 }
 
 int device_cu_count() {
@@ -59,14 +66,23 @@ int device_cu_count() {
 void run_gemm(GemmParams p, const GemmPlan& plan, bool swiglu, int64_t rows, int n_groups,
               hipStream_t stream) {
   const int64_t bound = max_tiles(rows, n_groups, plan.bm);
-  if (plan.grouped) launch_grouped(p, swiglu, bound, device_cu_count(), stream);
+  if (plan.eng == ENG_GROUPED) launch_grouped(p, swiglu, bound, device_cu_count(), stream);
   else launch_gemm_q4(p, plan.bm, swiglu, bound, stream);
+}
+
+void run_stream(StreamParams p, const GemmPlan& plan, bool swiglu, int64_t rows, int n_groups,
+                hipStream_t stream) {
+  const int64_t bound = max_tiles(rows, n_groups, plan.bm);
+  launch_stream(p, swiglu, plan.bm / 16, bound, device_cu_count(), stream);
 }
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, xsum_x, xsum_act, act, y, total;
+      tile_count, xsum_x, xsum_act, xprep, xc_x, xc_act, act, y, total;
 };
+
+// the streamed engine serves the layer when both GEMMs have K % 128 == 0
+bool layer_stream_ok(const moe_shape* s) { return s->d_model % 128 == 0 && s->d_ff % 128 == 0; }
 
 Layout make_layout(const moe_shape* s) {
   const int64_t T = s->T, D = s->d_model, E = s->n_experts, k = s->top_k, F = s->d_ff;
@@ -90,7 +106,11 @@ Layout make_layout(const moe_shape* s) {
   L.tile_count = take(16);
   L.xsum_x = take(T * (D / 64) * 4);
   L.xsum_act = take(rows_ext * (F / 64) * 4);
-  L.act = take(rows_ext * F * 2);
+  // prepared x (one zero row after the last) and the (-136 X, X) rows of x and act
+  L.xprep = take((T + 1) * D * 2);
+  L.xc_x = take((T + 1) * (D / 128) * 16);
+  L.xc_act = take((rows_ext + 1) * (F / 128) * 16);
+  L.act = take((rows_ext + 1) * F * 2);
   L.y = take(rows_ext * D * 2);
   L.total = o;
   return L;
@@ -151,14 +171,20 @@ moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout) {
 
 namespace {
 struct GemmWs {
-  size_t tiles, tile_count, xsum, total;
+  size_t tiles, tile_count, xsum, aprep, xc, total;
 };
 GemmWs gemm_ws(int32_t n_groups, int32_t rows_total, int32_t a_rows, int32_t K) {
   GemmWs w;
   w.tiles = 0;
   w.tile_count = align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4));
   w.xsum = w.tile_count + kAlign;
-  w.total = w.xsum + align_up((size_t)a_rows * (size_t)(K / 64) * 4);
+  w.aprep = w.xsum + align_up((size_t)a_rows * (size_t)(K / 64) * 4);
+  w.xc = w.aprep;
+  w.total = w.aprep;
+  if (K % 128 == 0) {  // the streamed engine's prepared copy of A
+    w.xc = w.aprep + align_up(((size_t)a_rows + 1) * (size_t)K * 2);
+    w.total = w.xc + align_up(((size_t)a_rows + 1) * (size_t)(K / 128) * 16);
+  }
   return w;
 }
 }  // namespace
@@ -259,12 +285,34 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
   if (!ws || ws_bytes < gw.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
 
-  const GemmPlan plan = plan_gemm(rows_total, n_groups);
+  const GemmPlan plan = plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows));
   int4* tiles = at<int4>(ws, gw.tiles);
   int32_t* tile_count = at<int32_t>(ws, gw.tile_count);
   float* xsum = at<float>(ws, gw.xsum);
-  if (plan.grouped) launch_row_group_sums(A, a_rows, K, xsum, stream);
   launch_build_tiles(offsets, n_groups, rows_total, plan.bm, tiles, tile_count, stream);
+  if (plan.eng == ENG_STREAM) {
+    uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
+    float4* xc = at<float4>(ws, gw.xc);
+    launch_prep(A, a_rows, K, aprep, xc, stream);
+    StreamParams sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.A = aprep;
+    sp.xc = xc;
+    sp.a_row_index = a_row_index;
+    sp.a_rows = a_rows;
+    sp.main = Q4Ptrs{W.q, W.scale, W.bias};
+    sp.n_main = n_groups;
+    sp.last = sp.main;
+    sp.N = N;
+    sp.K = K;
+    sp.C = C;
+    sp.ldc = epilogue == 1 ? N / 2 : N;
+    sp.tiles = tiles;
+    sp.tile_count = tile_count;
+    run_stream(sp, plan, epilogue == 1, rows_total, n_groups, stream);
+    return launch_status();
+  }
+  if (plan.eng == ENG_GROUPED) launch_row_group_sums(A, a_rows, K, xsum, stream);
 
   GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -350,10 +398,56 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
   permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
                has_shared ? T : -1, stream);
-  const GemmPlan plan = plan_gemm(rows, n_groups);
+  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape));
   launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
-  if (plan.grouped) launch_row_group_sums(x, T, D, xsum_x, stream);
+  if (plan.eng == ENG_STREAM) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), at<float4>(ws, L.xc_x), stream);
+  else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
+
+  if (plan.eng == ENG_STREAM) {
+    // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act (stored
+    // in the prepared column order, with its own (-136 X, X) rows for the down GEMM)
+    StreamParams sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.A = at<uint16_t>(ws, L.xprep);
+    sp.xc = at<float4>(ws, L.xc_x);
+    sp.a_row_index = sorted_tok;
+    sp.a_rows = T;
+    sp.main = Q4Ptrs{experts->gate_up.q, experts->gate_up.scale, experts->gate_up.bias};
+    sp.n_main = E;
+    sp.last = has_shared ? Q4Ptrs{shared->gate_up.q, shared->gate_up.scale, shared->gate_up.bias}
+                         : sp.main;
+    sp.N = 2 * F;
+    sp.K = D;
+    sp.C = act;
+    sp.ldc = F;
+    sp.c_perm = 1;
+    sp.xc_out = at<float4>(ws, L.xc_act);
+    sp.xc_out_ld = F / 128;
+    sp.tiles = tiles;
+    sp.tile_count = tile_count;
+    run_stream(sp, plan, true, rows, n_groups, stream);
+    mark(3);
+    // down: act rows in order -> y [rows, D]
+    sp.A = act;
+    sp.xc = at<float4>(ws, L.xc_act);
+    sp.a_row_index = nullptr;
+    sp.a_rows = rows;
+    sp.main = Q4Ptrs{experts->down.q, experts->down.scale, experts->down.bias};
+    sp.last = has_shared ? Q4Ptrs{shared->down.q, shared->down.scale, shared->down.bias} : sp.main;
+    sp.N = D;
+    sp.K = F;
+    sp.C = y;
+    sp.ldc = D;
+    sp.c_perm = 0;
+    sp.xc_out = nullptr;
+    run_stream(sp, plan, false, rows, n_groups, stream);
+    mark(4);
+    launch_combine(y, (int64_t)T * k, slot_row, wts,
+                   has_shared ? y + (int64_t)T * k * D : nullptr, out, T, D, k, stream);
+    mark(5);
+    return launch_status();
+  }
 
   // gate_up + SwiGLU: x rows gathered through sorted_tok -> act [rows, F]
   GemmParams p;

@@ -69,6 +69,36 @@ int grouped_slices(int N, bool swiglu);
 // out[r][g] = sum of A[r][64g .. 64g+63] in fp32, A bf16 [rows, K]
 void launch_row_group_sums(const uint16_t* A, int rows, int K, float* out, hipStream_t s);
 
+// Streamed engine (grouped_stream.hip): K % 128 == 0; A is the prepared copy (each
+// run of 8 columns stored in the order 0,4,1,5,2,6,3,7, one zero row after the
+// last, row a_rows) and xc holds per row and 128-K stage (-136 X_lo, -136 X_hi,
+// X_lo, X_hi) with X the row sums of the stage's two 64-wide groups.  Tiles of up to
+// 16 * nf rows (nf = 2 or 4; tile map built with bm = 16 * nf); one workgroup per
+// compute unit, persistent XCD-aware grid.
+struct StreamParams {
+  const uint16_t* A;          // prepared bf16 [a_rows + 1, K]
+  const float4* xc;           // [a_rows + 1, K / 128]
+  const int32_t* a_row_index; // nullable: identity
+  int32_t a_rows;             // >= 1
+  Q4Ptrs main;
+  int32_t n_main;
+  Q4Ptrs last;
+  int32_t N, K;
+  uint16_t* C;                // bf16 [rows, ldc]
+  int32_t ldc;
+  int32_t c_perm;             // store C in the prepared column order (SwiGLU only)
+  float4* xc_out;             // nullable; SwiGLU only: xc of C for the next GEMM
+  int32_t xc_out_ld;          // = (N / 2) / 128
+  const int4* tiles;
+  const int32_t* tile_count;
+  int32_t n_slices;
+};
+bool stream_supported(int N, int K, int a_rows);
+int stream_slices(int N, bool swiglu);
+void launch_prep(const uint16_t* A, int rows, int K, uint16_t* Ap, float4* xc, hipStream_t s);
+void launch_stream(StreamParams p, bool swiglu, int nf, int64_t n_tiles_bound, int n_cu,
+                   hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
                     const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);

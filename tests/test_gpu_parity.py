@@ -35,7 +35,7 @@ def torch_cuda():
     return torch
 
 
-ENGINES = ["rows", "grouped"]
+ENGINES = ["rows", "grouped", "stream"]
 
 
 @pytest.fixture
@@ -85,6 +85,8 @@ GEMM_INT_CASES = [
     ([200, 30], 256, 2048, True),            # 64-row tiles, every fragment count
     ([3, 0, 0, 9], 512, 512, False),
     ([127, 128, 129, 0, 300, 1], 384, 320, True),   # 128-row tiles: full, ragged, partial waves
+    ([127, 128, 129, 0, 300, 1], 384, 384, True),   # K % 128 == 0: streamed, 64-row tiles
+    ([5, 0, 70, 3], 320, 128, True),                # one 128-K stage per item
 ]
 
 
@@ -356,10 +358,10 @@ def test_layer_forward_parity_full(torch_cuda, name):
     _layer_full_check(torch_cuda, cfg)
 
 
-@pytest.mark.parametrize("engine", ["rows"], indirect=True)
+@pytest.mark.parametrize("engine", ["rows", "grouped"], indirect=True)
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_layer_forward_parity_full_rows(torch_cuda, name, engine):
-    """The same layers through the older register-streaming engine."""
+    """The same layers through the other two engines."""
     cfg = wl.CONFIGS[name]
     say(f"layer {name} [{engine}]: full oracle")
     _layer_full_check(torch_cuda, cfg)
@@ -408,7 +410,8 @@ def test_layer_forward_no_shared(torch_cuda):
 
 @pytest.mark.parametrize("engine", ENGINES, indirect=True)
 @pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192),
-                                   (1500, 320, 4, 2, 192)])
+                                   (1500, 320, 4, 2, 192), (1500, 256, 4, 2, 128),
+                                   (77, 384, 24, 3, 256), (5, 128, 16, 4, 128)])
 def test_layer_forward_odd_shapes(torch_cuda, shape, engine):
     """Wide top-k (k = 32), many experts (E = 1000), K % 128 == 64 (D = F = 192), a single expert
     per token."""
