@@ -31,26 +31,32 @@ moe_status check_shape(const moe_shape* s) {
 }
 
 // Which grouped-GEMM engine runs, and its tile rows.
-//   grouped (default): register-prefetched grouped engine, tiles of 32 rows;
-//   stream  (needs K % 128 == 0): operands streamed through an LDS ring by direct
-//           global->LDS loads; tiles of 32 rows, or 64 when groups average at
-//           least 48 rows;
-//   rows:   the first register-streaming engine, one workgroup per tile and slice.
-// The environment variable MOEQ4_GEMM=stream|grouped|rows forces one (for
-// measurement and tests; stream falls back to grouped where it does not apply).
-enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM };
+//   resident (default while groups average at most kResidentRows rows and the
+//            shapes allow it): tiles of up to 32 rows whose activations stay in LDS
+//            for the whole K while the weights stream through VGPRs;
+//   grouped  (default otherwise): register-prefetched grouped engine, tiles of 32 rows;
+//   stream   (needs K % 128 == 0): operands streamed through an LDS ring by direct
+//            global->LDS loads; tiles of 32 rows, or 64 when groups average at
+//            least 48 rows;
+//   rows:    the first register-streaming engine, one workgroup per tile and slice.
+// The environment variable MOEQ4_GEMM=resident|stream|grouped|rows forces one (for
+// measurement and tests; an engine that cannot take the shapes falls back to grouped).
+enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM, ENG_RESIDENT };
 struct GemmPlan {
   Engine eng;
   int bm;
 };
+constexpr int64_t kResidentRows = 64;
 
-GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok) {
+GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok) {
   const int64_t g = n_groups > 0 ? n_groups : 1;
   const char* env = getenv("MOEQ4_GEMM");
   if (env && strcmp(env, "rows") == 0) return GemmPlan{ENG_ROWS, rows <= 64 * g ? 32 : 64};
   if (env && strcmp(env, "grouped") == 0) return GemmPlan{ENG_GROUPED, kGroupedBM};
   if (env && strcmp(env, "stream") == 0 && stream_ok)
     return GemmPlan{ENG_STREAM, rows >= 48 * g ? 64 : 32};
+  if (env && strcmp(env, "resident") == 0 && resident_ok) return GemmPlan{ENG_RESIDENT, kResidentBM};
+  if (!env && resident_ok && rows <= kResidentRows * g) return GemmPlan{ENG_RESIDENT, kResidentBM};
   return GemmPlan{ENG_GROUPED, kGroupedBM};
 }
 
@@ -285,11 +291,39 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
   if (!ws || ws_bytes < gw.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
 
-  const GemmPlan plan = plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows));
+  const int n_cu = device_cu_count();
+  ResidentPlan rplan;
+  const bool resident_ok =
+      a_rows >= 1 &&
+      resident_plan(N, K, epilogue == 1, max_tiles(rows_total, n_groups, kResidentBM), n_cu, &rplan);
+  const GemmPlan plan =
+      plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows), resident_ok);
   int4* tiles = at<int4>(ws, gw.tiles);
   int32_t* tile_count = at<int32_t>(ws, gw.tile_count);
   float* xsum = at<float>(ws, gw.xsum);
   launch_build_tiles(offsets, n_groups, rows_total, plan.bm, tiles, tile_count, stream);
+  if (plan.eng == ENG_RESIDENT) {
+    // prepared copy of A (column order 0,4,1,5,... per run of 8, one zero row after the last)
+    uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
+    launch_prep(A, a_rows, K, aprep, nullptr, stream);
+    ResidentParams rp;
+    memset(&rp, 0, sizeof(rp));
+    rp.A = aprep;
+    rp.a_row_index = a_row_index;
+    rp.a_rows = a_rows;
+    rp.main = Q4Ptrs{W.q, W.scale, W.bias};
+    rp.n_main = n_groups;
+    rp.last = rp.main;
+    rp.N = N;
+    rp.K = K;
+    rp.C = C;
+    rp.ldc = epilogue == 1 ? N / 2 : N;
+    rp.c_perm = 0;
+    rp.tiles = tiles;
+    rp.tile_count = tile_count;
+    launch_resident(rp, rplan, epilogue == 1, stream);
+    return launch_status();
+  }
   if (plan.eng == ENG_STREAM) {
     uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
     float4* xc = at<float4>(ws, gw.xc);
@@ -398,11 +432,57 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
   permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
                has_shared ? T : -1, stream);
-  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape));
+  const int n_cu = device_cu_count();
+  const int64_t rbound = max_tiles(rows, n_groups, kResidentBM);
+  ResidentPlan rp_up, rp_down;
+  const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &rp_up) &&
+                           resident_plan(D, F, false, rbound, n_cu, &rp_down);
+  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok);
   launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
   if (plan.eng == ENG_STREAM) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), at<float4>(ws, L.xc_x), stream);
+  else if (plan.eng == ENG_RESIDENT) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), nullptr, stream);
   else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
+
+  if (plan.eng == ENG_RESIDENT) {
+    // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act, stored
+    // in the prepared column order so that the down GEMM reads it as is
+    ResidentParams rp;
+    memset(&rp, 0, sizeof(rp));
+    rp.A = at<uint16_t>(ws, L.xprep);
+    rp.a_row_index = sorted_tok;
+    rp.a_rows = T;
+    rp.main = Q4Ptrs{experts->gate_up.q, experts->gate_up.scale, experts->gate_up.bias};
+    rp.n_main = E;
+    rp.last = has_shared ? Q4Ptrs{shared->gate_up.q, shared->gate_up.scale, shared->gate_up.bias}
+                         : rp.main;
+    rp.N = 2 * F;
+    rp.K = D;
+    rp.C = act;
+    rp.ldc = F;
+    rp.c_perm = 1;
+    rp.tiles = tiles;
+    rp.tile_count = tile_count;
+    launch_resident(rp, rp_up, true, stream);
+    mark(3);
+    // down: act rows in order -> y [rows, D]
+    rp.A = act;
+    rp.a_row_index = nullptr;
+    rp.a_rows = rows;
+    rp.main = Q4Ptrs{experts->down.q, experts->down.scale, experts->down.bias};
+    rp.last = has_shared ? Q4Ptrs{shared->down.q, shared->down.scale, shared->down.bias} : rp.main;
+    rp.N = D;
+    rp.K = F;
+    rp.C = y;
+    rp.ldc = D;
+    rp.c_perm = 0;
+    launch_resident(rp, rp_down, false, stream);
+    mark(4);
+    launch_combine(y, (int64_t)T * k, slot_row, wts,
+                   has_shared ? y + (int64_t)T * k * D : nullptr, out, T, D, k, stream);
+    mark(5);
+    return launch_status();
+  }
 
   if (plan.eng == ENG_STREAM) {
     // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act (stored

@@ -1,0 +1,495 @@
+// Resident-tile grouped GEMM over groupwise-affine 4-bit weights for gfx950 (MI355X):
+// the engine for small groups (a few to a few dozen rows per expert), where the
+// layer is bound by streaming expert weights from HBM.
+//
+// Pages: MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference
+// engine for Qwen3.6-35B-A3B on Apple Silicon", body paragraph 5 (4-bit weights
+// with one bf16 scale and bias per 64, reconstructed tile by tile inside the
+// grouped GEMM with FP32 accumulation) and paragraph 7 (with little weight reuse,
+// memory bandwidth sets the ceiling).
+//
+// Arithmetic (exact up to fp32 rounding; no weight is rounded to bf16).  For output
+// row m, weight row n and one 64-wide group g with scale s and bias b:
+//   sum_c x[m,c] (s q[n,c] + b) = s * P' + (b - 128 s) * X,
+//   P' = sum_c x[m,c] (128 + q[n,c]),   X = sum_c x[m,c].
+// 128 + q is exactly the bf16 with bits 0x4300 | q (one AND-OR per pair of codes),
+// so P' is a bf16 matrix-core product with exact products.  X comes from the same
+// matrix cores, as the product of the activation fragment with a fragment of ones,
+// which leaves it in the accumulator layout of P'.  Each group then costs two FMAs
+// per output, whatever the bias.
+//
+// Work decomposition.  Tiles hold up to 32 rows of one group.  A tile's weight
+// rows are cut into chunks of 128 or 256 rows; the list of (tile, chunk) pairs is
+// split into equal contiguous ranges, one per workgroup, and the workgroups of one
+// XCD (workgroup b runs on XCD b % 8) take adjacent ranges, so the chunks of one
+// group run in one L2.  A workgroup walks its range tile by tile: it copies the
+// tile's activation rows for the whole K into LDS once (direct global->LDS loads,
+// rows gathered through the row index), then its eight wavefronts stream their
+// weight rows from HBM straight into VGPRs with 16-byte loads, up to three stages of
+// 256 K ahead, with no workgroup barrier inside the K loop.  A stage covers a whole
+// 128-byte line of every weight row it touches.  With K >= 1024 the eight wavefronts are
+// four column groups times two halves of K, and the halves are added through LDS
+// at the end of each chunk; otherwise eight column groups each take the whole K.
+// Each wavefront owns two 16-row weight fragments per chunk (SwiGLU: the gate
+// fragment and the matching up fragment), so equal work lands on every wavefront.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16): lane l supplies row l % 16 of A and
+// column l % 16 of B, each with the eight k-slots of quarter l / 16; the result
+// holds rows 4 (l / 16) + i, column l % 16.  In each 128-K half of a stage, quarter q
+// loads packed words 4q .. 4q+3 of its weight row; two permlane32 swaps between
+// lanes l and l ^ 32 regroup them so that each pair of MFMA steps draws all four
+// quarters' words from one scale group, and the A fragment of each step is read at
+// the LDS column of the word the lane holds.  A word unpacks to the k order
+// 0,4,1,5,2,6,3,7 and the activations are stored in that order.  LDS holds the activations as [fragment][16-byte
+// chunk][16 rows], which makes every fragment read a contiguous 256 bytes per
+// quarter-wave.
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moeq4 {
+
+namespace {
+
+constexpr int KS = 256;            // K per stage: four scale groups (two halves of 128)
+constexpr int SEG_CAP = 32;        // most tiles one workgroup may touch (host-checked)
+constexpr int PART_BYTES = 16384;  // partial sums / output staging
+constexpr uint32_t kMagic = 0x43004300u;
+constexpr uint32_t kNib = 0x000F000Fu;
+constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+
+__host__ __device__ constexpr int part_off(int K) { return 2 * (K / 8) * 256; }
+__host__ __device__ constexpr int seg_off(int K) { return part_off(K) + PART_BYTES; }
+__host__ __device__ constexpr int idx_off(int K) { return seg_off(K) + SEG_CAP * 16; }
+__host__ __device__ constexpr int lds_bytes(int K) { return idx_off(K) + SEG_CAP * 32 * 4; }
+static_assert(lds_bytes(kResidentMaxK) <= 160 * 1024, "LDS budget");
+
+// kMagic in a VGPR the compiler cannot constant-fold, so that (v & mask) | magic is
+// one v_and_or_b32; only VALU instructions read it.
+__device__ __forceinline__ uint32_t opaque_magic() {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "n"(kMagic));
+  return v;
+}
+
+__device__ __forceinline__ u32x4_t unpack_word(uint32_t w, uint32_t magic) {
+  u32x4_t b;
+  b[0] = (w & kNib) | magic;
+  b[1] = ((w >> 4) & kNib) | magic;
+  b[2] = ((w >> 8) & kNib) | magic;
+  b[3] = ((w >> 12) & kNib) | magic;
+  return b;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld(const void* base, uint32_t byte_off) {
+  return *(const T*)((const char*)base + byte_off);
+}
+
+// s_waitcnt vmcnt(0) with the other counters unconstrained, fenced against reordering
+__device__ __forceinline__ void wait_vmcnt0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations only,
+// not for its in-flight weight loads (a __syncthreads() would drain those).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// natural column c (0..7) of an 8-column run -> its position in the order 0,4,1,5,...
+__device__ __forceinline__ int perm8(int c) { return ((c & 3) << 1) | (c >> 2); }
+
+// Weights of one 256-K stage for one lane: for each of its two fragment rows and each
+// 128-K half, the packed words 4q .. 4q+3 (one 16-byte load), and the scales and
+// biases of the stage's four groups (8 bytes each).
+struct StageW {
+  u32x4_t c[2][2];  // [fragment][half]
+  u32x2_t s[2], b[2];
+};
+
+// The two permlane32 swaps (word 0 <-> 2, word 1 <-> 3 between lanes l and l ^ 32) of a
+// lane's word quad.  Before them quarter q holds words 4q .. 4q+3 of a 128-K half; after
+// them MFMA steps 0, 1 draw every quarter's word from one scale group and steps 2, 3
+// from the other.  The word a lane holds in each step is tracked by applying the same
+// swaps to the word numbers, so nothing depends on the swap's direction.
+__device__ __forceinline__ u32x4_t swap_quad(u32x4_t v) {
+  const auto r0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  u32x4_t o;
+  o[0] = r0[0];
+  o[1] = r1[0];
+  o[2] = r0[1];
+  o[3] = r1[1];
+  return o;
+}
+
+template <bool SWIGLU, int NST>
+__device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned char* smem) {
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = l & 15, q = l >> 4;
+  const int N = p.N, K = p.K, KW = K >> 3, KG = K >> 6;
+  const int S = p.ksplit;                 // 1 or 2 (host-chosen)
+  const int CGN = 8 / S;                  // column groups
+  const int cg = wave % CGN, kp = wave / CGN;
+  const int CR = 32 * CGN;                // weight rows per chunk
+  const int NCH = N / CR;
+  constexpr int D = NST % 4 == 0 ? 4 : NST % 2 == 0 ? 2 : 1;  // stages in flight
+  const int kbase = kp * NST;             // this wavefront's K stages: kbase .. kbase + NST - 1
+  const int A_FRAG = KW * 256;
+  unsigned char* part = smem + part_off(K);
+  int4* segt = (int4*)(smem + seg_off(K));
+  int* idxt = (int*)(smem + idx_off(K));
+
+  // ---- this workgroup's range of (tile, chunk) pairs
+  const int cnt = *p.tile_count;
+  const int G = gridDim.x;
+  const int rank = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int64_t total = (int64_t)cnt * NCH;
+  const int c_begin = (int)(total * rank / G), c_end = (int)(total * (rank + 1) / G);
+  if (c_begin >= c_end) return;  // uniform, before any barrier
+  const int t_first = c_begin / NCH;
+  const int nseg = (c_end - 1) / NCH - t_first + 1;
+  if (nseg > SEG_CAP) return;    // excluded by the host; never write past the table
+  // tiles and activation row indices of every segment, before any weight load
+  for (int e = tid; e < nseg * 32; e += 512) {
+    const int k = e >> 5, rr = e & 31;
+    const int4 t = p.tiles[t_first + k];
+    if (rr == 0) segt[k] = t;
+    const int row = t.y + (rr < t.z ? rr : t.z - 1);
+    int a = p.a_row_index ? p.a_row_index[row] : row;
+    if (a < 0 || a >= p.a_rows) a = p.a_rows;  // the zero row
+    idxt[e] = a;
+  }
+  __syncthreads();
+
+  auto seg_of = [&](int ch) -> int4 {
+    const int k = ch / NCH - t_first;
+    const int4 t = segt[k];
+    return make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
+                     __builtin_amdgcn_readfirstlane(t.z), k);
+  };
+
+  // ---- weight prefetch cursor (stream of this wavefront's stages over its chunks)
+  int pf_ch = c_begin, pf_s = 0;
+  const uint32_t* pf_q = nullptr;
+  const uint16_t* pf_sc = nullptr;
+  const uint16_t* pf_bi = nullptr;
+  uint32_t pf_co[2], pf_so[2];
+  auto pf_chunk = [&]() __attribute__((always_inline)) {
+    const int4 t = seg_of(pf_ch);
+    const int cin = pf_ch - (pf_ch / NCH) * NCH;
+    const int g = t.x;
+    const bool in_main = g < p.n_main;
+    const int gi = in_main ? g : 0;
+    pf_q = (in_main ? p.main.q : p.last.q) + (int64_t)gi * N * KW;
+    pf_sc = (in_main ? p.main.s : p.last.s) + (int64_t)gi * N * KG;
+    pf_bi = (in_main ? p.main.b : p.last.b) + (int64_t)gi * N * KG;
+    int n0, n1;
+    if (SWIGLU) {
+      const int u = CGN * cin + cg;
+      n0 = 16 * u + m;
+      n1 = (N >> 1) + 16 * u + m;
+    } else {
+      n0 = CR * cin + 32 * cg + m;
+      n1 = n0 + 16;
+    }
+    pf_co[0] = ((uint32_t)n0 * KW + 4 * q) * 4u;
+    pf_co[1] = ((uint32_t)n1 * KW + 4 * q) * 4u;
+    pf_so[0] = (uint32_t)n0 * KG * 2u;
+    pf_so[1] = (uint32_t)n1 * KG * 2u;
+  };
+  auto pf_load = [&](StageW& w) __attribute__((always_inline)) {
+    const int st = kbase + pf_s;
+    const uint32_t* qs = pf_q + 32 * st;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      w.c[j][0] = ld<u32x4_t>(qs, pf_co[j]);
+      w.c[j][1] = ld<u32x4_t>(qs + 16, pf_co[j]);
+      w.s[j] = ld<u32x2_t>(pf_sc + 4 * st, pf_so[j]);
+      w.b[j] = ld<u32x2_t>(pf_bi + 4 * st, pf_so[j]);
+    }
+    if (++pf_s == NST) {
+      pf_s = 0;
+      if (++pf_ch < c_end) pf_chunk();
+    }
+  };
+
+  const uint32_t magic = opaque_magic();
+  const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  // word held in MFMA step t of a 128-K half, after the swaps
+  uint32_t widx[4] = {(uint32_t)(4 * q), (uint32_t)(4 * q + 1), (uint32_t)(4 * q + 2),
+                      (uint32_t)(4 * q + 3)};
+  {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(widx[0], widx[2], false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(widx[1], widx[3], false, false);
+    widx[0] = r0[0];
+    widx[2] = r0[1];
+    widx[1] = r1[0];
+    widx[3] = r1[1];
+  }
+  // scale group (0 or 1 within the half) of steps 0, 1 and of steps 2, 3: uniform
+  const int gsel0 = __builtin_amdgcn_readfirstlane((int)(widx[0] >> 3));
+  const int gsel1 = __builtin_amdgcn_readfirstlane((int)(widx[2] >> 3));
+  // LDS byte offset of this lane's A fragment row for each step (chunk = word of the half)
+  uint32_t a_step[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a_step[t] = widx[t] * 256u + 16u * m;
+
+  f32x4_t acc[2][2];  // [row fragment][weight fragment]
+
+  // one 256-K stage: halves hh of 128 K, each two MFMA step pairs (one scale group each)
+  auto compute = [&](const StageW& w, int st, auto nf_tag) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const unsigned char* ab = smem + ((uint32_t)st * 2 + hh) * 4096u;
+      u32x4_t wsw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wsw[j] = swap_quad(w.c[j][hh]);
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int gs = pr ? gsel1 : gsel0;  // group within the half
+        float sc[2], cb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t sw = w.s[j][hh], bw = w.b[j][hh];
+          sc[j] = gs ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
+          const float bj = gs ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
+          cb[j] = fmaf(-128.f, sc[j], bj);
+        }
+        u32x4_t av[NF][2];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            av[f][h] = *(const u32x4_t*)(ab + f * A_FRAG + a_step[2 * pr + h]);
+        f32x4_t X[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          X[f] = mfma16x16x32(av[f][1], ones, mfma16x16x32(av[f][0], ones, zero));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4_t B0 = unpack_word(wsw[j][2 * pr], magic);
+          const u32x4_t B1 = unpack_word(wsw[j][2 * pr + 1], magic);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const f32x4_t P = mfma16x16x32(av[f][1], B1, mfma16x16x32(av[f][0], B0, zero));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[f][j][i] = fmaf(sc[j], P[i], fmaf(cb[j], X[f][i], acc[f][j][i]));
+          }
+        }
+      }
+    }
+  };
+
+  // ---- prologue: D - 1 stages in flight.  Every wavefront issues the same loads for
+  // every stage, also past the end of its stream (those reload a valid stage and are
+  // never used), so that the compiler's wait counts stay exact across the loop.
+  StageW W[D];
+  pf_chunk();
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) pf_load(W[d]);
+
+  // One chunk: NST stages in steps of D; stage s uses register set s % D (NST % D == 0).
+  // The loads stay outside the branch on the fragment count: identical loads in both
+  // arms would be merged into the join block, after the matrix work, which would turn
+  // the prefetch into load-then-wait.
+  auto run_chunk = [&](int nfv) __attribute__((always_inline)) {
+#pragma nounroll
+    for (int sb = 0; sb < NST; sb += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        pf_load(W[(d + D - 1) % D]);
+        if (nfv == 2) compute(W[d], kbase + sb + d, std::integral_constant<int, 2>{});
+        else compute(W[d], kbase + sb + d, std::integral_constant<int, 1>{});
+      }
+    }
+  };
+
+  int cur_seg = -1;
+  for (int ch = c_begin; ch < c_end; ++ch) {
+    const int4 t = seg_of(ch);
+    const int k = t.w, row0 = t.y, nrows = t.z;
+    const int nfv = nrows > 16 ? 2 : 1;
+    const int cin = ch - (ch / NCH) * NCH;
+    if (k != cur_seg) {
+      // the tile's activation rows for the whole K: fragment f, 16-byte chunks
+      // 4 cb .. 4 cb + 3 of its 16 rows per direct load (1 KB of LDS)
+      if (cur_seg >= 0) lds_barrier();  // every wavefront is done with the previous tile
+      const int per_f = K >> 5;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (f < nfv) {
+          const int arow = idxt[k * 32 + 16 * f + m];
+          const uint16_t* src = p.A + (int64_t)arow * K + 8 * q;
+          for (int cb = wave; cb < per_f; cb += 8)
+            __builtin_amdgcn_global_load_lds(src + 32 * cb, smem + f * A_FRAG + cb * 1024, 16, 0,
+                                             0);
+        }
+      }
+      wait_vmcnt0();
+      lds_barrier();
+      cur_seg = k;
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[f][j] = zero;
+    run_chunk(nfv);
+
+    // ---- end of chunk: halves of K meet through LDS, then bf16 rows go out
+    bool owner = true;
+    unsigned char* stg = part + wave * 2048;
+    if (S == 2) {
+      f32x4_t* pw = (f32x4_t*)(part + cg * 4096) + l;
+      lds_barrier();  // the previous chunk's partial sums have been consumed
+      if (kp == 1) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          if (f < nfv) {
+            pw[(2 * f + 0) * 64] = acc[f][0];
+            pw[(2 * f + 1) * 64] = acc[f][1];
+          }
+      }
+      lds_barrier();
+      owner = kp == 0;
+      if (owner) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          if (f < nfv) {
+            const f32x4_t o0 = pw[(2 * f + 0) * 64], o1 = pw[(2 * f + 1) * 64];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[f][0][i] += o0[i];
+              acc[f][1][i] += o1[i];
+            }
+          }
+      }
+      stg = part + cg * 4096;
+    }
+    if (owner) {
+      uint16_t* cs = (uint16_t*)stg;
+      if (SWIGLU) {
+        // 16 output columns: silu(gate) * up, in the prepared column order if asked
+        const int col = p.c_perm ? ((m & 8) | perm8(m & 7)) : m;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          if (f < nfv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gte = acc[f][0][i], up = acc[f][1][i];
+              const float h = gte / (1.f + __expf(-gte)) * up;
+              cs[(16 * f + 4 * q + i) * 16 + col] = to_bf16(h);
+            }
+          }
+        const int r = l >> 1, half = l & 1;
+        const int u = CGN * cin + cg;
+        if (r < nrows)
+          *(u32x4_t*)(p.C + (int64_t)(row0 + r) * p.ldc + 16 * u + 8 * half) =
+              *(const u32x4_t*)(cs + r * 16 + 8 * half);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          if (f < nfv) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                cs[(16 * f + 4 * q + i) * 32 + 16 * j + m] = to_bf16(acc[f][j][i]);
+          }
+        const int col0 = CR * cin + 32 * cg;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int r = (64 * pp + l) >> 2, piece = l & 3;
+          if (r < nrows)
+            *(u32x4_t*)(p.C + (int64_t)(row0 + r) * p.ldc + col0 + 8 * piece) =
+                *(const u32x4_t*)(cs + r * 32 + 8 * piece);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <bool SWIGLU, int NST>
+__global__ __launch_bounds__(512, 1) void q4_resident_kernel(ResidentParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_dyn[];
+  resident_body<SWIGLU, NST>(p, smem_dyn);
+}
+
+namespace {
+
+template <bool SWIGLU, int NST>
+void launch_one(const ResidentParams& p, int grid, hipStream_t s) {
+  const int bytes = lds_bytes(p.K);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)q4_resident_kernel<SWIGLU, NST>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(kResidentMaxK));
+    attr = true;
+  }
+  hipLaunchKernelGGL((q4_resident_kernel<SWIGLU, NST>), dim3(grid), dim3(512), bytes, s, p);
+}
+
+template <bool SWIGLU>
+void launch_nst(const ResidentParams& p, int nst, int grid, hipStream_t s) {
+  switch (nst) {
+    case 1: launch_one<SWIGLU, 1>(p, grid, s); break;
+    case 2: launch_one<SWIGLU, 2>(p, grid, s); break;
+    case 3: launch_one<SWIGLU, 3>(p, grid, s); break;
+    case 4: launch_one<SWIGLU, 4>(p, grid, s); break;
+    case 5: launch_one<SWIGLU, 5>(p, grid, s); break;
+    case 6: launch_one<SWIGLU, 6>(p, grid, s); break;
+    case 7: launch_one<SWIGLU, 7>(p, grid, s); break;
+    default: launch_one<SWIGLU, 8>(p, grid, s); break;
+  }
+}
+
+}  // namespace
+
+bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, ResidentPlan* out) {
+  (void)swiglu;
+  if (K <= 0 || K % KS != 0 || K > kResidentMaxK || N <= 0) return false;
+  const int KP = K / KS;  // 256-K stages
+  int S = (KP % 2 == 0 && KP >= 4) ? 2 : 1;
+  if (N % (32 * (8 / S)) != 0) {
+    if (S == 1 && KP % 2 == 0 && N % 128 == 0) S = 2;
+    else return false;
+  }
+  const int nst = KP / S;
+  if (nst < 1 || nst > kResidentMaxStages) return false;
+  int grid = (n_cu > 0 ? n_cu : 256) / 8 * 8;
+  if (grid < 8) grid = 8;
+  const int64_t NCH = N / (32 * (8 / S));
+  const int64_t chunks = (n_tiles_bound > 0 ? n_tiles_bound : 1) * NCH;
+  const int64_t per_wg = (chunks + grid - 1) / grid;
+  const int64_t segs = (per_wg - 1) / NCH + 2;
+  if (segs > SEG_CAP) return false;
+  if (out) {
+    out->ksplit = S;
+    out->stages = nst;
+    out->grid = grid;
+  }
+  return true;
+}
+
+void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hipStream_t s) {
+  p.ksplit = plan.ksplit;
+  if (swiglu) launch_nst<true>(p, plan.stages, plan.grid, s);
+  else launch_nst<false>(p, plan.stages, plan.grid, s);
+}
+
+}  // namespace moeq4

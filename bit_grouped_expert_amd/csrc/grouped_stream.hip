@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
       o[2] = (v[1] & 0xFFFFu) | (v[3] << 16);
       o[3] = (v[1] >> 16) | (v[3] & 0xFFFF0000u);
       *(u32x4_t*)(Ap + (int64_t)r * K + 8 * c) = o;
-      if ((c & 7) == 0) {
+      if (xc && (c & 7) == 0) {
         const int g = c >> 3;  // 64-wide group
         float* o4 = (float*)(xc + (int64_t)r * KP + (g >> 1));
         o4[g & 1] = -136.f * sum;

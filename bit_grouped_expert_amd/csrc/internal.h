@@ -99,6 +99,41 @@ void launch_prep(const uint16_t* A, int rows, int K, uint16_t* Ap, float4* xc, h
 void launch_stream(StreamParams p, bool swiglu, int nf, int64_t n_tiles_bound, int n_cu,
                    hipStream_t s);
 
+// Resident-tile engine (grouped_resident.hip), for small groups: tiles of up to 32
+// rows (tile map built with bm = 32) whose activation rows stay in LDS for the whole
+// K.  A is the prepared copy (each run of 8 columns stored in the order
+// 0,4,1,5,2,6,3,7) and row a_rows of A must be readable: rows that fall outside
+// [0, a_rows) read it, so it must be zero where that can happen.  C rows are written with 16-byte stores (ldc % 8 == 0).
+// With SwiGLU (N = 2F) and c_perm set, C is stored in the prepared column order.
+constexpr int kResidentBM = 32;
+constexpr int kResidentMaxK = 2048;
+struct ResidentParams {
+  const uint16_t* A;          // prepared bf16 [a_rows (+1), K]
+  const int32_t* a_row_index; // nullable: identity
+  int32_t a_rows;
+  Q4Ptrs main;
+  int32_t n_main;
+  Q4Ptrs last;
+  int32_t N, K;
+  uint16_t* C;
+  int32_t ldc;
+  int32_t c_perm;
+  const int4* tiles;
+  const int32_t* tile_count;
+  int32_t ksplit;             // set by launch_resident
+};
+constexpr int kResidentMaxStages = 8;  // 256-K stages per wavefront and chunk
+struct ResidentPlan {
+  int ksplit;  // 1: eight column groups over the whole K; 2: four column groups x two K halves
+  int stages;  // 256-K stages per wavefront and chunk (K / 256 / ksplit)
+  int grid;    // workgroups (a multiple of 8)
+};
+// false when the engine cannot take the shape (K % 256, K > kResidentMaxK, more than
+// kResidentMaxStages stages per wavefront, N not a multiple of the chunk, or too many
+// tiles per workgroup for n_tiles_bound)
+bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, ResidentPlan* out);
+void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
                     const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);

@@ -35,7 +35,7 @@ def torch_cuda():
     return torch
 
 
-ENGINES = ["rows", "grouped", "stream"]
+ENGINES = ["rows", "grouped", "stream", "resident"]
 
 
 @pytest.fixture
@@ -87,6 +87,10 @@ GEMM_INT_CASES = [
     ([127, 128, 129, 0, 300, 1], 384, 320, True),   # 128-row tiles: full, ragged, partial waves
     ([127, 128, 129, 0, 300, 1], 384, 384, True),   # K % 128 == 0: streamed, 64-row tiles
     ([5, 0, 70, 3], 320, 128, True),                # one 128-K stage per item
+    ([0, 1, 17, 33, 100], 256, 1024, True),         # two halves of K, two 256-K stages each
+    ([5, 0, 70, 3, 16], 512, 1536, False),          # halves of three stages, no prefetch
+    ([1, 31, 32, 33], 768, 256, False),             # one stage over the whole K
+    ([40, 2, 0, 27], 256, 512, True),               # whole K per wavefront, two stages
 ]
 
 
@@ -358,10 +362,10 @@ def test_layer_forward_parity_full(torch_cuda, name):
     _layer_full_check(torch_cuda, cfg)
 
 
-@pytest.mark.parametrize("engine", ["rows", "grouped"], indirect=True)
+@pytest.mark.parametrize("engine", ["rows", "grouped", "stream"], indirect=True)
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_layer_forward_parity_full_rows(torch_cuda, name, engine):
-    """The same layers through the other two engines."""
+    """The same layers through the engines the default does not pick for them."""
     cfg = wl.CONFIGS[name]
     say(f"layer {name} [{engine}]: full oracle")
     _layer_full_check(torch_cuda, cfg)
@@ -411,7 +415,8 @@ def test_layer_forward_no_shared(torch_cuda):
 @pytest.mark.parametrize("engine", ENGINES, indirect=True)
 @pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192),
                                    (1500, 320, 4, 2, 192), (1500, 256, 4, 2, 128),
-                                   (77, 384, 24, 3, 256), (5, 128, 16, 4, 128)])
+                                   (77, 384, 24, 3, 256), (5, 128, 16, 4, 128),
+                                   (300, 512, 24, 3, 256), (40, 1024, 64, 4, 512)])
 def test_layer_forward_odd_shapes(torch_cuda, shape, engine):
     """Wide top-k (k = 32), many experts (E = 1000), K % 128 == 64 (D = F = 192), a single expert
     per token."""
