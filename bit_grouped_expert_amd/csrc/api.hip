@@ -217,7 +217,7 @@ static moe_status route_impl(const moe_shape* shape, const uint16_t* x, const fl
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
   launch_router_split(router_w, Rs, E, D, stream);
-  launch_router_logits(x, Rs, logits, T, D, E, stream);
+  launch_router_logits(x, Rs, logits, T, D, E, nullptr, stream);
   launch_topk(logits, x, router_w, T, D, E, k, gap, topk_idx, topk_w, stream);
   return launch_status();
 }
@@ -421,26 +421,33 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   auto mark = [&](int i) {
     if (events && events[i]) hipEventRecord(events[i], stream);
   };
-  // routing
-  mark(0);
-  uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
-  float* logits = at<float>(ws, L.logits);
-  launch_router_split(router_w, Rs, E, D, stream);
-  launch_router_logits(x, Rs, logits, T, D, E, stream);
-  launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
-  mark(1);
-  // histogram, scan, scatter (+ identity rows of the shared group), tile map
-  permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
-               has_shared ? T : -1, stream);
+  // the GEMM engine depends only on the shapes: chosen first, so that the router can
+  // write the resident engine's copy of x on the way
   const int n_cu = device_cu_count();
   const int64_t rbound = max_tiles(rows, n_groups, kResidentBM);
   ResidentPlan rp_up, rp_down;
   const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &rp_up) &&
                            resident_plan(D, F, false, rbound, n_cu, &rp_down);
   const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok);
-  launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
+  // routing
+  mark(0);
+  uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
+  float* logits = at<float>(ws, L.logits);
+  launch_router_split(router_w, Rs, E, D, stream);
+  launch_router_logits(x, Rs, logits, T, D, E,
+                       plan.eng == ENG_RESIDENT ? at<uint16_t>(ws, L.xprep) : nullptr, stream);
+  launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
+  mark(1);
+  // histogram, scan, scatter (+ identity rows of the shared group), tile map
+  if (permute_small_ok(T, E)) {
+    launch_permute_small(idx, T, k, E, offsets, sorted_tok, slot_row, has_shared ? T : -1,
+                         plan.bm, tiles, tile_count, stream);
+  } else {
+    permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
+                 has_shared ? T : -1, stream);
+    launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
+  }
   if (plan.eng == ENG_STREAM) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), at<float4>(ws, L.xc_x), stream);
-  else if (plan.eng == ENG_RESIDENT) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), nullptr, stream);
   else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
 

@@ -39,6 +39,17 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// 8 bf16 values (x0..x7, two per dword) -> the order x0,x4,x1,x5,x2,x6,x3,x7, in which
+// a packed word of eight 4-bit codes unpacks.
+__device__ __forceinline__ u32x4_t interleave8(u32x4_t d) {
+  u32x4_t o;
+  o[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
+  o[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
+  o[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
+  o[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
+  return o;
+}
+
 // Butterfly exchange with the lane `lane ^ mask` (ds_bpermute based).
 __device__ __forceinline__ uint32_t xor_u32(uint32_t v, int mask) {
   int src = (lane_id() ^ mask) << 2;

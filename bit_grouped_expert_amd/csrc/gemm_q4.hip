@@ -47,16 +47,6 @@ constexpr int LDA = KC + 8;     // LDS row stride in bf16 (16-byte pad against b
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
 constexpr uint32_t kMask = 0x000F000Fu;
 
-// 8 bf16 activations (x0..x7 in two-per-dword order) -> order x0,x4,x1,x5,x2,x6,x3,x7.
-__device__ __forceinline__ u32x4_t interleave8(u32x4_t d) {
-  u32x4_t o;
-  o[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
-  o[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
-  o[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
-  o[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
-  return o;
-}
-
 // One packed word of eight codes -> MFMA operand holding 128 + q in the order 0,4,1,5,2,6,3,7.
 __device__ __forceinline__ u32x4_t unpack_word(uint32_t w) {
   u32x4_t b;

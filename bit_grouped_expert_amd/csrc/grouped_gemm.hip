@@ -73,16 +73,6 @@ static_assert(BMX * LDC_PLAIN <= 2 * A_BUF, "output staging must fit the A buffe
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
 constexpr uint32_t kNib = 0x000F000Fu;
 
-// 8 bf16 activations (x0..x7 two per dword) -> order x0,x4,x1,x5,x2,x6,x3,x7.
-__device__ __forceinline__ u32x4_t interleave8(u32x4_t d) {
-  u32x4_t o;
-  o[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
-  o[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
-  o[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
-  o[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
-  return o;
-}
-
 // (v & mask) | magic.  `magic` is kept in a VGPR the compiler cannot constant-fold
 // (see opaque_magic), so that this becomes one v_and_or_b32 with the mask in an SGPR
 // instead of a separate AND and OR (a GFX9 VOP3 cannot encode two literals).

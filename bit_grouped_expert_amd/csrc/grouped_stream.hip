@@ -514,12 +514,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     sum += __shfl_xor(sum, 2);
     sum += __shfl_xor(sum, 4);
     if (c < nch) {
-      u32x4_t o;
-      o[0] = (v[0] & 0xFFFFu) | (v[2] << 16);
-      o[1] = (v[0] >> 16) | (v[2] & 0xFFFF0000u);
-      o[2] = (v[1] & 0xFFFFu) | (v[3] << 16);
-      o[3] = (v[1] >> 16) | (v[3] & 0xFFFF0000u);
-      *(u32x4_t*)(Ap + (int64_t)r * K + 8 * c) = o;
+      *(u32x4_t*)(Ap + (int64_t)r * K + 8 * c) = interleave8(v);
       if (xc && (c & 7) == 0) {
         const int g = c >> 3;  // 64-wide group
         float* o4 = (float*)(xc + (int64_t)r * KP + (g >> 1));

@@ -9,8 +9,10 @@ namespace moeq4 {
 
 // ---------------------------------------------------------------- routing
 void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t s);
+// xprep (nullable): also write the prepared copy of x ([T + 1, D], last row zero) read by
+// the resident-tile GEMM
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
-                          hipStream_t s);
+                          uint16_t* xprep, hipStream_t s);
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
                  float tau, int32_t* idx, float* w, hipStream_t s);
 
@@ -55,6 +57,12 @@ inline int64_t max_tiles(int64_t rows_total, int n_groups, int bm) {
 }
 void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
                         int32_t* tile_count, hipStream_t s);
+// Histogram, scan, stable scatter and tile map in one single-workgroup launch (T <= 1024).
+// Same results as launch_count + launch_scan + launch_scatter + launch_build_tiles.
+bool permute_small_ok(int T, int E);
+void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,
+                          int4* tiles, int32_t* tile_count, hipStream_t s);
 // bm: 32 or 64 rows per tile.  Grid = max_tiles(rows_total, n_groups, bm) * n_slices.
 void launch_gemm_q4(GemmParams p, int bm, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
 int gemm_q4_slices(int N, bool swiglu);

@@ -158,17 +158,17 @@ void launch_scatter(const int32_t* idx, int T, int k, int E, const int32_t* chun
 // [0, rows_total] so that no tile leaves C, and at most `cap` tiles are written
 // (cap = the bound the grid was sized with), so malformed offsets cannot
 // overrun the tile array.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                           int n_groups, int rows_total, int bm,
-                                                           int4* __restrict__ tiles, int cap,
-                                                           int32_t* __restrict__ tile_count) {
+// Tile map over group boundaries offs[0..n_groups] (read from global memory or LDS);
+// every thread of a 1024-thread workgroup calls it.
+__device__ void write_tiles(const int32_t* offs, int n_groups, int rows_total, int bm,
+                            int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
   int running = 0;
   for (int g0 = 0; g0 < n_groups; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     int lo = 0, n = 0;
     if (g < n_groups) {
-      lo = min(max(offsets[g], 0), rows_total);
-      int hi = min(max(offsets[g + 1], lo), rows_total);
+      lo = min(max(offs[g], 0), rows_total);
+      int hi = min(max(offs[g + 1], lo), rows_total);
       n = hi - lo;
     }
     const int nt = (n + bm - 1) / bm;
@@ -181,11 +181,102 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   if (threadIdx.x == 0) *tile_count = min(running, cap);
 }
 
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                           int n_groups, int rows_total, int bm,
+                                                           int4* __restrict__ tiles, int cap,
+                                                           int32_t* __restrict__ tile_count) {
+  write_tiles(offsets, n_groups, rows_total, bm, tiles, cap, tile_count);
+}
+
 void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
                         int32_t* tile_count, hipStream_t s) {
   const int cap = (int)max_tiles(rows_total, n_groups, bm);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, n_groups, rows_total,
                      bm, tiles, cap, tile_count);
+}
+
+// ---------------------------------------------------------------------------- fused (T <= 1024)
+// One workgroup of 1024 threads, thread t = token t: the histogram, the scan, the
+// stable scatter and the tile map of a small batch in one launch.  Same ranking as
+// the chunked kernels above: a token's rank among the tokens of expert e is the
+// popcount of the lower waves' bit masks for e plus the bits of lower lanes in its
+// own wave.  With shared_rows >= 0 the shared group's rows follow at T * k.
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_row, int shared_rows, int bm,
+    int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
+  extern __shared__ unsigned long long masks[];  // [16 waves][E], then offs[E + 2]
+  int32_t* offs = (int32_t*)(masks + 16 * E);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
+  __syncthreads();
+  const unsigned long long bit = 1ull << lane;
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
+    }
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < 16; ++w) cnt += __popcll(masks[w * E + tid]);
+  int total;
+  const int excl = block_exclusive_scan_1024(cnt, &total);
+  if (tid < E) {
+    offs[tid] = excl;
+    offsets[tid] = excl;
+  }
+  if (tid == 0) {
+    offs[E] = total;
+    offsets[E] = total;
+    if (shared_rows >= 0) {
+      offs[E + 1] = total + shared_rows;
+      offsets[E + 1] = total + shared_rows;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      int32_t row = -1;
+      if (e >= 0 && e < E) {
+        int rank = __popcll(masks[wave * E + e] & (bit - 1ull));
+        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+        row = offs[e] + rank;
+        if (row >= 0 && row < T * k) sorted_tok[row] = tid;  // always true for consistent counts
+        else row = -1;
+      }
+      slot_row[(int64_t)tid * k + j] = row;
+    }
+    if (shared_rows >= 0) sorted_tok[T * k + tid] = tid;
+  }
+  const int n_groups = E + (shared_rows >= 0 ? 1 : 0);
+  const int rows_total = T * k + (shared_rows >= 0 ? shared_rows : 0);
+  write_tiles(offs, n_groups, rows_total, bm, tiles, cap, tile_count);
+}
+
+constexpr size_t small_lds(int E) { return 16 * (size_t)E * 8 + (size_t)(E + 2) * 4; }
+constexpr int kSmallMaxE = 1024;  // the largest expert count the shape check admits
+static_assert(small_lds(kSmallMaxE) + 64 <= 160 * 1024, "LDS budget");
+
+bool permute_small_ok(int T, int E) { return T >= 1 && T <= 1024 && E <= kSmallMaxE; }
+
+void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,
+                          int4* tiles, int32_t* tile_count, hipStream_t s) {
+  const int n_groups = E + (shared_rows >= 0 ? 1 : 0);
+  const int rows_total = T * k + (shared_rows >= 0 ? shared_rows : 0);
+  const int cap = (int)max_tiles(rows_total, n_groups, bm);
+  const size_t lds = small_lds(E);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)permute_small_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)small_lds(kSmallMaxE));
+    attr = true;
+  }
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, idx, T, k, E, offsets,
+                     sorted_tok, slot_row, shared_rows, bm, tiles, cap, tile_count);
 }
 
 }  // namespace moeq4

@@ -49,68 +49,79 @@ void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t
 }
 
 // ---------------------------------------------------------------------------- logits
-// Workgroup tile: TM tokens x 64 experts; wave w owns experts e0 + 16w .. +15.
-// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (l % 16) and the
-// eight k-slots 8*(l/16)..+7; the accumulator holds rows 4*(l/16)+i, column l%16.
-template <int TM>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+// Workgroup tile: 16 tokens x 32 experts.  Its eight wavefronts are two 16-expert
+// tiles times four quarters of D; each keeps one accumulator per R plane (three
+// independent MFMA chains) and loads four 32-wide k-steps ahead of their use.  The
+// quarters are added through LDS.  v_mfma_f32_16x16x32_bf16 layout: lane l supplies
+// row (l % 16) and the eight k-slots 8*(l/16)..+7; the accumulator holds rows
+// 4*(l/16)+i, column l % 16.
+//
+// With `xprep` set, the workgroups of the first expert column also write the copy of x
+// that the resident-tile GEMM reads (each run of 8 columns in the order
+// 0,4,1,5,2,6,3,7, plus one zero row after the last token), from the x fragments they
+// load anyway.
+__global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ Rs,
                                                             float* __restrict__ L, int T, int D,
-                                                            int E) {
-  constexpr int NT = TM / 16;
+                                                            int E, uint16_t* __restrict__ xprep) {
+  __shared__ f32x4_t red[4][2][64];
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 15, q = l >> 4;
-  const int t0 = blockIdx.x * TM;
-  const int e0 = blockIdx.y * 64 + wave * 16;
-  if (e0 >= E) return;  // this kernel has no barriers
-  const int e = e0 + m;
+  const int tile = wave & 1, kq = wave >> 1;
+  const int t0 = blockIdx.x * 16;
+  const int e = blockIdx.y * 32 + 16 * tile + m;
   const bool ev = e < E;
+  const int t = t0 + m;
+  const bool tv = t < T;
   const int64_t plane = (int64_t)E * D;
   const uint16_t* rb = Rs + (int64_t)(ev ? e : 0) * D + 8 * q;
-  const uint16_t* xa[NT];
-  bool tv[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    int t = t0 + 16 * i + m;
-    tv[i] = t < T;
-    xa[i] = x + (int64_t)(tv[i] ? t : 0) * D + 8 * q;
-  }
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* xa = x + (int64_t)(tv ? t : 0) * D + 8 * q;
+  const int nsteps = D >> 5;
+  const int s0 = nsteps * kq / 4, s1 = nsteps * (kq + 1) / 4;
+  const bool prep = xprep != nullptr && blockIdx.y == 0 && tile == 0;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < D; k0 += 32) {
-    u32x4_t b0 = ev ? *(const u32x4_t*)(rb + k0) : zero;
-    u32x4_t b1 = ev ? *(const u32x4_t*)(rb + plane + k0) : zero;
-    u32x4_t b2 = ev ? *(const u32x4_t*)(rb + 2 * plane + k0) : zero;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      u32x4_t a = tv[i] ? *(const u32x4_t*)(xa[i] + k0) : zero;
-      acc[i] = mfma16x16x32(a, b0, acc[i]);
-      acc[i] = mfma16x16x32(a, b1, acc[i]);
-      acc[i] = mfma16x16x32(a, b2, acc[i]);
-    }
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll 4
+  for (int st = s0; st < s1; ++st) {
+    const int k0 = 32 * st;
+    const u32x4_t xv = tv ? *(const u32x4_t*)(xa + k0) : zero;
+    const u32x4_t b0 = ev ? *(const u32x4_t*)(rb + k0) : zero;
+    const u32x4_t b1 = ev ? *(const u32x4_t*)(rb + plane + k0) : zero;
+    const u32x4_t b2 = ev ? *(const u32x4_t*)(rb + 2 * plane + k0) : zero;
+    a0 = mfma16x16x32(xv, b0, a0);
+    a1 = mfma16x16x32(xv, b1, a1);
+    a2 = mfma16x16x32(xv, b2, a2);
+    if (prep && tv) *(u32x4_t*)(xprep + (int64_t)t * D + k0 + 8 * q) = interleave8(xv);
   }
-  if (!ev) return;
+  if (xprep && blockIdx.x == 0 && blockIdx.y == 0 && tile == 1) {
+    // the zero row after the last token
+    for (int c = kq * 64 + l; c < (D >> 3); c += 256)
+      *(u32x4_t*)(xprep + (int64_t)T * D + 8 * c) = zero;
+  }
+  f32x4_t acc;
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int i = 0; i < 4; ++i) acc[i] = a0[i] + (a1[i] + a2[i]);
+  if (kq > 0) red[kq][tile][l] = acc;
+  __syncthreads();
+  if (kq == 0 && ev) {
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      const f32x4_t o = red[j][tile][l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += o[i];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int t = t0 + 16 * i + 4 * q + r;
-      if (t < T) L[(int64_t)t * E + e] = acc[i][r];
+      const int tt = t0 + 4 * q + r;
+      if (tt < T) L[(int64_t)tt * E + e] = acc[r];
     }
+  }
 }
 
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
-                          hipStream_t s) {
-  dim3 block(256);
-  if (T >= 2048) {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    hipLaunchKernelGGL(router_logits_kernel<64>, grid, block, 0, s, x, Rs, L, T, D, E);
-  } else {
-    dim3 grid((T + 15) / 16, (E + 63) / 64);
-    hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, 0, s, x, Rs, L, T, D, E);
-  }
+                          uint16_t* xprep, hipStream_t s) {
+  dim3 grid((T + 15) / 16, (E + 31) / 32), block(512);
+  hipLaunchKernelGGL(router_logits_kernel, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
 }
 
 // ---------------------------------------------------------------------------- top-k
