@@ -60,7 +60,9 @@ constexpr uint32_t kNib = 0x000F000Fu;
 constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
 __host__ __device__ constexpr int part_off(int K) { return 2 * (K / 8) * 256; }
-__host__ __device__ constexpr int seg_off(int K) { return part_off(K) + PART_BYTES; }
+// row sums X of the tile's activations per 64-wide group, fp32 [K / 64][32 rows]
+__host__ __device__ constexpr int xs_off(int K) { return part_off(K) + PART_BYTES; }
+__host__ __device__ constexpr int seg_off(int K) { return xs_off(K) + (K / 64) * 32 * 4; }
 __host__ __device__ constexpr int idx_off(int K) { return seg_off(K) + SEG_CAP * 16; }
 __host__ __device__ constexpr int lds_bytes(int K) { return idx_off(K) + SEG_CAP * 32 * 4; }
 static_assert(lds_bytes(kResidentMaxK) <= 160 * 1024, "LDS budget");
@@ -132,7 +134,7 @@ __device__ __forceinline__ u32x4_t swap_quad(u32x4_t v) {
   return o;
 }
 
-template <bool SWIGLU, int NST>
+template <bool SWIGLU, int NST, int GS>
 __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned char* smem) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,7 +145,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   const int cg = wave % CGN, kp = wave / CGN;
   const int CR = 32 * CGN;                // weight rows per chunk
   const int NCH = N / CR;
-  constexpr int D = NST % 4 == 0 ? 4 : NST % 2 == 0 ? 2 : 1;  // stages in flight
+  constexpr int D = NST;  // register sets: the next D - 1 stages are in flight
   const int kbase = kp * NST;             // this wavefront's K stages: kbase .. kbase + NST - 1
   const int A_FRAG = KW * 256;
   unsigned char* part = smem + part_off(K);
@@ -238,9 +240,6 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     widx[1] = r1[0];
     widx[3] = r1[1];
   }
-  // scale group (0 or 1 within the half) of steps 0, 1 and of steps 2, 3: uniform
-  const int gsel0 = __builtin_amdgcn_readfirstlane((int)(widx[0] >> 3));
-  const int gsel1 = __builtin_amdgcn_readfirstlane((int)(widx[2] >> 3));
   // LDS byte offset of this lane's A fragment row for each step (chunk = word of the half)
   uint32_t a_step[4];
 #pragma unroll
@@ -248,49 +247,75 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 
   f32x4_t acc[2][2];  // [row fragment][weight fragment]
 
-  // one 256-K stage: halves hh of 128 K, each two MFMA step pairs (one scale group each)
-  auto compute = [&](const StageW& w, int st, auto nf_tag) __attribute__((always_inline)) {
+  // One 256-K stage in two 128-K halves.  In a half, MFMA steps 2 (g ^ GS) and
+  // 2 (g ^ GS) + 1 take scale group g of the half (GS: the group order the swaps
+  // produce, uniform and fixed by the hardware; both orders are compiled).  Each half
+  // runs in three phases kept apart by scheduling barriers, so that matrix results are
+  // consumed only after all of the half's chains are issued: operands (LDS reads and
+  // unpacked weights), then the MFMA chains, then acc += s * P'.  The bias term
+  // (b - 128 s) X is not applied here: lane quarter q keeps (b - 128 s) of group q of
+  // the stage for the fp32 matrix-core product at the end of the chunk.
+  auto compute = [&](const StageW& w, int st, float* cbq, auto nf_tag) __attribute__((always_inline)) {
     constexpr int NF = decltype(nf_tag)::value;
+    // (b - 128 s) of group q of this stage (q = lane quarter), both weight fragments
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t sw = (q & 2) ? w.s[j][1] : w.s[j][0];
+      const uint32_t bw = (q & 2) ? w.b[j][1] : w.b[j][0];
+      const float sq = (q & 1) ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
+      const float bq = (q & 1) ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
+      cbq[j] = fmaf(-128.f, sq, bq);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const unsigned char* ab = smem + ((uint32_t)st * 2 + hh) * 4096u;
-      u32x4_t wsw[2];
+      u32x4_t av[2][NF][2];  // [group][row fragment][half step]
 #pragma unroll
-      for (int j = 0; j < 2; ++j) wsw[j] = swap_quad(w.c[j][hh]);
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int gs = pr ? gsel1 : gsel0;  // group within the half
-        float sc[2], cb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t sw = w.s[j][hh], bw = w.b[j][hh];
-          sc[j] = gs ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
-          const float bj = gs ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
-          cb[j] = fmaf(-128.f, sc[j], bj);
-        }
-        u32x4_t av[NF][2];
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            av[f][h] = *(const u32x4_t*)(ab + f * A_FRAG + a_step[2 * pr + h]);
-        f32x4_t X[NF];
+            av[g][f][h] = *(const u32x4_t*)(ab + f * A_FRAG + a_step[2 * (g ^ GS) + h]);
+      u32x4_t B[2][2][2];  // [group][weight fragment][half step]
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t wsw = swap_quad(w.c[j][hh]);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) B[g][j][h] = unpack_word(wsw[2 * (g ^ GS) + h], magic);
+      }
+      float sc[2][2];  // [group][weight fragment]
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sc[0][j] = bf16lo_to_f32(w.s[j][hh]);
+        sc[1][j] = bf16hi_to_f32(w.s[j][hh]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t P[2][2][NF];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
-          X[f] = mfma16x16x32(av[f][1], ones, mfma16x16x32(av[f][0], ones, zero));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4_t B0 = unpack_word(wsw[j][2 * pr], magic);
-          const u32x4_t B1 = unpack_word(wsw[j][2 * pr + 1], magic);
+          for (int j = 0; j < 2; ++j) P[g][j][f] = mfma16x16x32(av[g][f][0], B[g][j][0], zero);
 #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            const f32x4_t P = mfma16x16x32(av[f][1], B1, mfma16x16x32(av[f][0], B0, zero));
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[f][j][i] = fmaf(sc[j], P[i], fmaf(cb[j], X[f][i], acc[f][j][i]));
-          }
-        }
-      }
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) P[g][j][f] = mfma16x16x32(av[g][f][1], B[g][j][1], P[g][j][f]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(sc[g][j], P[g][j][f][i], acc[f][j][i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -302,19 +327,36 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) pf_load(W[d]);
 
-  // One chunk: NST stages in steps of D; stage s uses register set s % D (NST % D == 0).
-  // The loads stay outside the branch on the fragment count: identical loads in both
-  // arms would be merged into the join block, after the matrix work, which would turn
-  // the prefetch into load-then-wait.
+  // One chunk: NST stages, stage s on register set s (D == NST, so the rotation starts
+  // over with every chunk).  The loads stay outside the branch on the fragment count:
+  // identical loads in both arms would be merged into the join block, after the matrix
+  // work, which would turn the prefetch into load-then-wait.  cbk[s][j]: the lane's
+  // (b - 128 s) of stage s, kept for the bias product.
+  float cbk[NST][2];
   auto run_chunk = [&](int nfv) __attribute__((always_inline)) {
-#pragma nounroll
-    for (int sb = 0; sb < NST; sb += D) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        pf_load(W[(d + D - 1) % D]);
-        if (nfv == 2) compute(W[d], kbase + sb + d, std::integral_constant<int, 2>{});
-        else compute(W[d], kbase + sb + d, std::integral_constant<int, 1>{});
-      }
+    for (int d = 0; d < D; ++d) {
+      pf_load(W[(d + D - 1) % D]);
+      if (nfv == 2) compute(W[d], kbase + d, cbk[d], std::integral_constant<int, 2>{});
+      else compute(W[d], kbase + d, cbk[d], std::integral_constant<int, 1>{});
+    }
+  };
+  // acc += sum over this wavefront's groups of (b - 128 s) X, on the fp32 matrix cores
+  // (v_mfma_f32_16x16x4_f32: lane l gives A[row l % 16][k = l / 16] and
+  // B[k = l / 16][column l % 16]): step s takes the four groups of stage s, k = group.
+  const float* xs = (const float*)(smem + xs_off(K));
+  auto bias_term = [&](int nfv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < NST; ++d) {
+      const int g = 4 * (kbase + d) + q;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        if (f < nfv) {
+          const float xa = xs[g * 32 + 16 * f + m];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, cbk[d][j], acc[f][j], 0, 0, 0);
+        }
     }
   };
 
@@ -341,6 +383,21 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       }
       wait_vmcnt0();
       lds_barrier();
+      // X[group][row] of the tile: the product of each group's two 32-K activation
+      // fragments with a fragment of ones, written by the lanes of column 0
+      {
+        float* xw = (float*)(smem + xs_off(K));
+        const int KG4 = K >> 6;
+        for (int pi = wave; pi < nfv * KG4; pi += 8) {
+          const int f = pi / KG4, g = pi - f * KG4;
+          const unsigned char* ab = smem + f * A_FRAG + (8 * g + 2 * q) * 256 + 16 * m;
+          const u32x4_t a0 = *(const u32x4_t*)ab;
+          const u32x4_t a1 = *(const u32x4_t*)(ab + 256);
+          const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
+          if (m == 0) *(f32x4_t*)(xw + g * 32 + 16 * f + 4 * q) = X;
+        }
+      }
+      lds_barrier();
       cur_seg = k;
     }
 #pragma unroll
@@ -348,6 +405,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[f][j] = zero;
     run_chunk(nfv);
+    bias_term(nfv);
 
     // ---- end of chunk: halves of K meet through LDS, then bf16 rows go out
     bool owner = true;
@@ -424,10 +482,18 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 
 }  // namespace
 
+// GS: scale group of MFMA steps 0 and 1 after the word swaps (0 or 1), the same on
+// every lane and every call; read off the swapped word numbers on entry, and both
+// orders are compiled, so the result never depends on the swap's direction.
 template <bool SWIGLU, int NST>
 __global__ __launch_bounds__(512, 1) void q4_resident_kernel(ResidentParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_dyn[];
-  resident_body<SWIGLU, NST>(p, smem_dyn);
+  const int l = threadIdx.x & 63;
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
+                                                  false, false);
+  const int gs = __builtin_amdgcn_readfirstlane((int)(r[0] >> 3));
+  if (gs) resident_body<SWIGLU, NST, 1>(p, smem_dyn);
+  else resident_body<SWIGLU, NST, 0>(p, smem_dyn);
 }
 
 namespace {
@@ -450,11 +516,7 @@ void launch_nst(const ResidentParams& p, int nst, int grid, hipStream_t s) {
     case 1: launch_one<SWIGLU, 1>(p, grid, s); break;
     case 2: launch_one<SWIGLU, 2>(p, grid, s); break;
     case 3: launch_one<SWIGLU, 3>(p, grid, s); break;
-    case 4: launch_one<SWIGLU, 4>(p, grid, s); break;
-    case 5: launch_one<SWIGLU, 5>(p, grid, s); break;
-    case 6: launch_one<SWIGLU, 6>(p, grid, s); break;
-    case 7: launch_one<SWIGLU, 7>(p, grid, s); break;
-    default: launch_one<SWIGLU, 8>(p, grid, s); break;
+    default: launch_one<SWIGLU, 4>(p, grid, s); break;
   }
 }
 

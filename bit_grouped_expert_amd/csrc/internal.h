@@ -130,7 +130,7 @@ struct ResidentParams {
   const int32_t* tile_count;
   int32_t ksplit;             // set by launch_resident
 };
-constexpr int kResidentMaxStages = 8;  // 256-K stages per wavefront and chunk
+constexpr int kResidentMaxStages = 4;  // 256-K stages per wavefront and chunk
 struct ResidentPlan {
   int ksplit;  // 1: eight column groups over the whole K; 2: four column groups x two K halves
   int stages;  // 256-K stages per wavefront and chunk (K / 256 / ksplit)
