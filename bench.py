@@ -32,11 +32,20 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, AMD published
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
+# the gate_up kernel the library picks for each workload (engine chosen by group size)
+KERNEL_LABEL = {
+    "prefill512": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
+    "decode1": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
+    "decode4": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
+}
+
 # counters of a plain copy kernel of known size, read in the same rocprofv3 --pmc runs
 # as the gate_up kernel (KiB per dispatch); None until profiled
 TRAFFIC = {
-    # config: {"fetch_kib": ..., "write_kib": ..., "copy_fetch_kib": ..., "copy_write_kib": ...,
-    #          "copy_bytes": ...}
+    # rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over `bench.py --config prefill512 --steps 2
+    # --warmup 1 --no-cpu-baseline --copy-probe` (summary in profiles/)
+    "prefill512": {"fetch_kib": 172412.3, "write_kib": 4608.5,
+                   "copy_fetch_kib": 524325.4, "copy_write_kib": 1048576.0, "copy_bytes": 2 ** 30},
 }
 
 
@@ -125,33 +134,35 @@ def main():
         lw = sets[i % len(sets)]
         L.moe_layer_forward(shp, xd, rd, lw.experts, lw.shared, out, ws, stream=stream)
 
+    # HIP events recorded by the library on the layer's stream at the stage boundaries of
+    # every timed step (torch creates a HIP event on its first record: record them all once)
+    nst = L.N_STAGE_EVENTS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    def step_events(i):
+        lw = sets[i % len(sets)]
+        L.moe_layer_forward_events(shp, xd, rd, lw.experts, lw.shared, out, ws, evs[i],
+                                   stream=stream)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"bench: warmup done ({args.warmup} steps)")
 
-    # ---- timed region: exactly K steps
+    # ---- timed region: exactly K steps, each with its stage events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step_events(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     log(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
-    # ---- per-stage durations: HIP events recorded by the library on the same stream
-    nst = L.N_STAGE_EVENTS
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
-    for row in evs:          # torch creates the HIP event on its first record
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        lw = sets[i % len(sets)]
-        L.moe_layer_forward_events(shp, xd, rd, lw.experts, lw.shared, out, ws, evs[i],
-                                   stream=stream)
-    torch.cuda.synchronize()
     names = ["route", "permute", "gate_up", "down", "combine"]
     stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
@@ -176,7 +187,7 @@ def main():
         roof["traffic"] = t["fetch_kib"] * 1024 * scale_f + t["write_kib"] * 1024 * scale_w
     else:
         roof["traffic"] = None
-    roof["kernel"] = "grouped gate_up + SwiGLU (q4_grouped_kernel)"
+    roof["kernel"] = KERNEL_LABEL.get(cfg.name, "grouped gate_up + SwiGLU")
     roof["algorithmic_bytes"] = gb
     roof["algorithmic_flops"] = gf
     roof["kernel_us"] = gu_s * 1e6
