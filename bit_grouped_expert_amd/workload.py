@@ -21,7 +21,11 @@ Recipe (all numpy PCG64):
                          over all G = E+1 groups at once (group E = shared expert):
                          codes: uniform random uint32 words [G, N, K/8], i.e. eight
                          independent uniform 4-bit codes per word;
-                         scale = bf16_rne(|N(0, 0.02)|) [G, N, K/64]; bias = -8*scale.
+                         scale = bf16_rne(|N(0, 0.02)|) [G, N, K/64];
+                         bias = bf16_rne(-scale * (7.5 + 0.5 z)), z = N(0, 1) per group
+                         (the bias of an affine 4-bit quantiser is the group's minimum,
+                         near -7.5 scales for normal weights; drawn per group, so it is
+                         not tied to the scale).
   skewed routing:        x[:, 0] = 1 and R[e, 0] = beta_e with
                          beta_e = -0.242 * ln(e+1) (Zipf-like popularity) and
                          beta_e = -1e4 for the last 4 experts (forced empty groups).
@@ -130,7 +134,8 @@ def _q4_matrix(rng, G, N, K):
     q = rng.integers(0, 2**32, size=(G, N, K // 8), dtype=np.uint32)
     s32 = np.abs(rng.standard_normal((G, N, K // GROUP), dtype=np.float32) * np.float32(0.02))
     scale = f32_to_bf16_bits(s32)
-    bias = f32_to_bf16_bits(np.float32(-8.0) * bf16_bits_to_f32(scale))
+    z = rng.standard_normal((G, N, K // GROUP), dtype=np.float32)
+    bias = f32_to_bf16_bits(-bf16_bits_to_f32(scale) * (np.float32(7.5) + np.float32(0.5) * z))
     return q, scale, bias
 
 

@@ -145,8 +145,8 @@ def test_grouped_gemm_exact_integer(torch_cuda, case, bias_val, engine):
 @pytest.mark.parametrize("epilogue", [0, 1])
 @pytest.mark.parametrize("counts", [[0, 3, 16, 29, 64, 90, 1], [250, 0, 131, 7, 384]])
 def test_grouped_gemm_float_vs_oracle(torch_cuda, epilogue, counts, free_bias, engine):
-    """Float weights: the generator's (bias = -8 scale) and, with free_bias, general affine
-    weights whose bias is drawn independently of the scale."""
+    """Float weights: the generator's (bias = -scale * (7.5 + 0.5 z) per group) and, with
+    free_bias, biases drawn independently of the scale and of either sign."""
     torch = torch_cuda
     rng = np.random.default_rng(7 + epilogue)
     say(f"float gemm [{engine}] epilogue={epilogue} counts={counts} free_bias={free_bias}")

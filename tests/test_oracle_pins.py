@@ -280,8 +280,10 @@ def test_zero_codes_give_shared_only():
     cfg = wl.MoEConfig("z", 8, 128, 4, 2, 64)
     x, router = wl.make_activations(cfg, 0)
     w = wl.make_weights(cfg, 1000)
-    for key in ("gate_up_q", "down_q"):
-        w[key][:cfg.E] = 0x88888888
+    for key in ("gate_up", "down"):
+        w[key + "_q"][:cfg.E] = 0x88888888
+        s = oracle.bf16_to_f64(w[key + "_s"][:cfg.E])
+        w[key + "_b"][:cfg.E] = wl.f32_to_bf16_bits((-8.0 * s).astype(np.float32))
     res = oracle.moe_layer(x, router, w, cfg.k)
     assert np.all(res["Y"] == 0)
     assert np.array_equal(res["out"], res["S"])
@@ -309,7 +311,11 @@ def test_generator_recipe():
     assert w["gate_up_q"].shape == (17, 256, 32) and w["gate_up_s"].shape == (17, 256, 4)
     assert w["down_q"].shape == (17, 256, 16) and w["down_s"].shape == (17, 256, 2)
     s = oracle.bf16_to_f64(w["gate_up_s"])
-    assert np.all(s >= 0) and np.array_equal(oracle.bf16_to_f64(w["gate_up_b"]), -8 * s)
+    b = oracle.bf16_to_f64(w["gate_up_b"])
+    assert np.all(s >= 0)
+    ratio = -b[s > 0] / s[s > 0]          # bias = -scale * (7.5 + 0.5 z), bf16-rounded
+    assert abs(ratio.mean() - 7.5) < 0.05 and 0.4 < ratio.std() < 0.6
+    assert not np.array_equal(b, -8 * s)
     codes = oracle.unpack_codes(w["down_q"])
     hist = np.bincount(codes.ravel(), minlength=16)
     assert hist.min() > 0.9 * codes.size / 16
