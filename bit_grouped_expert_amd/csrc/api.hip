@@ -31,9 +31,9 @@ moe_status check_shape(const moe_shape* s) {
 }
 
 // Which grouped-GEMM engine runs, and its tile rows.
-//   resident (default while groups average at most kResidentRows rows and the
-//            shapes allow it): tiles of up to 32 rows whose activations stay in LDS
-//            for the whole K while the weights stream through VGPRs;
+//   resident (default wherever the shapes allow it): tiles of up to 32 rows whose
+//            activations stay in LDS for the whole K while the weights stream
+//            through VGPRs (measured faster than grouped at 512 and at 8192 tokens);
 //   grouped  (default otherwise): register-prefetched grouped engine, tiles of 32 rows;
 //   stream   (needs K % 128 == 0): operands streamed through an LDS ring by direct
 //            global->LDS loads; tiles of 32 rows, or 64 when groups average at
@@ -46,8 +46,6 @@ struct GemmPlan {
   Engine eng;
   int bm;
 };
-constexpr int64_t kResidentRows = 64;
-
 GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok) {
   const int64_t g = n_groups > 0 ? n_groups : 1;
   const char* env = getenv("MOEQ4_GEMM");
@@ -56,7 +54,7 @@ GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok)
   if (env && strcmp(env, "stream") == 0 && stream_ok)
     return GemmPlan{ENG_STREAM, rows >= 48 * g ? 64 : 32};
   if (env && strcmp(env, "resident") == 0 && resident_ok) return GemmPlan{ENG_RESIDENT, kResidentBM};
-  if (!env && resident_ok && rows <= kResidentRows * g) return GemmPlan{ENG_RESIDENT, kResidentBM};
+  if (!env && resident_ok) return GemmPlan{ENG_RESIDENT, kResidentBM};
   return GemmPlan{ENG_GROUPED, kGroupedBM};
 }
 
@@ -100,7 +98,7 @@ Layout make_layout(const moe_shape* s) {
     o = align_up(o + bytes);
     return at;
   };
-  L.rsplit = take(3 * E * D * 2);
+  L.rsplit = take(3 * (size_t)((E + 15) / 16 * 16) * D * 2);
   L.logits = take(T * E * 4);
   L.topk_idx = take(T * k * 4);
   L.topk_w = take(T * k * 4);

@@ -205,8 +205,11 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_row, int shared_rows, int bm,
     int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
-  extern __shared__ unsigned long long masks[];  // [16 waves][E], then offs[E + 2]
-  int32_t* offs = (int32_t*)(masks + 16 * E);
+  // [16 waves][E] masks, then [16 waves][E] base rows (offset of the expert plus the
+  // tokens of the lower waves), then offs[E + 2]
+  extern __shared__ unsigned long long masks[];
+  int32_t* base = (int32_t*)(masks + 16 * E);
+  int32_t* offs = base + 16 * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
   __syncthreads();
@@ -219,13 +222,19 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   }
   __syncthreads();
   int cnt = 0;
-  if (tid < E)
-    for (int w = 0; w < 16; ++w) cnt += __popcll(masks[w * E + tid]);
+  int pre[16];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    pre[w] = cnt;
+    if (tid < E) cnt += __popcll(masks[w * E + tid]);
+  }
   int total;
   const int excl = block_exclusive_scan_1024(cnt, &total);
   if (tid < E) {
     offs[tid] = excl;
     offsets[tid] = excl;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) base[w * E + tid] = excl + pre[w];
   }
   if (tid == 0) {
     offs[E] = total;
@@ -241,9 +250,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
       const int e = idx[(int64_t)tid * k + j];
       int32_t row = -1;
       if (e >= 0 && e < E) {
-        int rank = __popcll(masks[wave * E + e] & (bit - 1ull));
-        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
-        row = offs[e] + rank;
+        row = base[wave * E + e] + __popcll(masks[wave * E + e] & (bit - 1ull));
         if (row >= 0 && row < T * k) sorted_tok[row] = tid;  // always true for consistent counts
         else row = -1;
       }
@@ -256,8 +263,10 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   write_tiles(offs, n_groups, rows_total, bm, tiles, cap, tile_count);
 }
 
-constexpr size_t small_lds(int E) { return 16 * (size_t)E * 8 + (size_t)(E + 2) * 4; }
-constexpr int kSmallMaxE = 1024;  // the largest expert count the shape check admits
+constexpr size_t small_lds(int E) {
+  return 16 * (size_t)E * 8 + 16 * (size_t)E * 4 + (size_t)(E + 2) * 4;
+}
+constexpr int kSmallMaxE = 768;  // above, the chunked kernels run
 static_assert(small_lds(kSmallMaxE) + 64 <= 160 * 1024, "LDS budget");
 
 bool permute_small_ok(int T, int E) { return T >= 1 && T <= 1024 && E <= kSmallMaxE; }

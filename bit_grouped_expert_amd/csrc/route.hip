@@ -20,108 +20,210 @@
 // fp64) and the top k of those, by fp64 logit, are chosen.  Any expert outside
 // that set has a true logit below k+1 candidates' as long as the fp32 error is
 // under tau/2, so the selection equals the exact (fp64) top-k.
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
 namespace moeq4 {
 
 // ---------------------------------------------------------------------------- split
+// The planes are written fragment-major: for each 16-expert tile `et` and 32-wide
+// k-step `s`, the 64 lanes' 16-byte operands of v_mfma_f32_16x16x32_bf16 lie in one
+// contiguous kilobyte, lane l = m + 16 q holding expert 16 et + m, k = 32 s + 8 q .. +7.
+// Plane p starts at p * Epad * D (Epad = E rounded up to 16; padding experts are zero),
+// so every operand load of the logits kernel reads one contiguous kilobyte.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ R,
-                                                           uint16_t* __restrict__ Rs, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    float r = R[i];
-    uint16_t h0 = to_bf16(r);
-    float r1 = r - bf16lo_to_f32(h0);
-    uint16_t h1 = to_bf16(r1);
-    float r2 = r1 - bf16lo_to_f32(h1);
-    uint16_t h2 = to_bf16(r2);
-    Rs[i] = h0;
-    Rs[n + i] = h1;
-    Rs[2 * n + i] = h2;
+                                                           uint16_t* __restrict__ Rs, int E, int D) {
+  const int nsteps = D >> 5, ET = (E + 15) >> 4;
+  const int64_t nfrag = (int64_t)ET * nsteps * 64, plane = (int64_t)ET * 16 * D;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nfrag; i += (int64_t)gridDim.x * 256) {
+    const int l = (int)(i & 63);
+    const int64_t ts = i >> 6;
+    const int s = (int)(ts % nsteps), et = (int)(ts / nsteps);
+    const int e = 16 * et + (l & 15), k0 = 32 * s + 8 * (l >> 4);
+    float r[8];
+    if (e < E) {
+      const f32x4_t lo = *(const f32x4_t*)(R + (int64_t)e * D + k0);
+      const f32x4_t hi = *(const f32x4_t*)(R + (int64_t)e * D + k0 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r[j] = lo[j];
+        r[4 + j] = hi[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = 0.f;
+    }
+    uint32_t h[3][4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t p0[3], p1[3];
+      float a = r[j], b = r[j + 1];
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const uint16_t ha = to_bf16(a), hb = to_bf16(b);
+        p0[pl] = ha;
+        p1[pl] = hb;
+        a -= bf16lo_to_f32(ha);
+        b -= bf16lo_to_f32(hb);
+      }
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) h[pl][j >> 1] = p0[pl] | (p1[pl] << 16);
+    }
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl)
+      *(u32x4_t*)(Rs + pl * plane + i * 8) = u32x4_t{h[pl][0], h[pl][1], h[pl][2], h[pl][3]};
   }
 }
 
 void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t s) {
-  int64_t n = (int64_t)E * D;
-  int blocks = (int)((n + 255) / 256);
+  const int64_t nfrag = (int64_t)((E + 15) / 16) * (D / 32) * 64;
+  int blocks = (int)((nfrag + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(router_split_kernel, dim3(blocks), dim3(256), 0, s, R, Rs, n);
+  hipLaunchKernelGGL(router_split_kernel, dim3(blocks), dim3(256), 0, s, R, Rs, E, D);
 }
 
 // ---------------------------------------------------------------------------- logits
-// Workgroup tile: 16 tokens x 32 experts.  Its eight wavefronts are two 16-expert
-// tiles times four quarters of D; each keeps one accumulator per R plane (three
-// independent MFMA chains) and loads four 32-wide k-steps ahead of their use.  The
-// quarters are added through LDS.  v_mfma_f32_16x16x32_bf16 layout: lane l supplies
-// row (l % 16) and the eight k-slots 8*(l/16)..+7; the accumulator holds rows
-// 4*(l/16)+i, column l % 16.
+// Workgroup tile: 16 NTF tokens x 32 experts.  Its eight wavefronts are two 16-expert
+// tiles times four quarters of D; each keeps one accumulator per R plane and token
+// fragment (independent MFMA chains), and its loads are unconditional (rows past T or E
+// are clamped to valid rows and their results dropped), so that the unrolled loop
+// keeps several 32-wide k-steps of loads in flight.  The quarters are added through
+// LDS.  NTF = 4 at large T shares each R fragment among four token fragments.
+// v_mfma_f32_16x16x32_bf16 layout: lane l supplies row (l % 16) and the eight k-slots
+// 8*(l/16)..+7; the accumulator holds rows 4*(l/16)+i, column l % 16.
 //
 // With `xprep` set, the workgroups of the first expert column also write the copy of x
 // that the resident-tile GEMM reads (each run of 8 columns in the order
-// 0,4,1,5,2,6,3,7, plus one zero row after the last token), from the x fragments they
-// load anyway.
+// 0,4,1,5,2,6,3,7, plus one zero row after the last token): their tile-0 wavefronts
+// store each x fragment as they use it.
+template <int NTF>
 __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ Rs,
                                                             float* __restrict__ L, int T, int D,
                                                             int E, uint16_t* __restrict__ xprep) {
-  __shared__ f32x4_t red[4][2][64];
+  __shared__ f32x4_t red[3][2][NTF][64];
+  static_assert(NTF == 1 || NTF == 4, "token fragments");
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 15, q = l >> 4;
   const int tile = wave & 1, kq = wave >> 1;
-  const int t0 = blockIdx.x * 16;
-  const int e = blockIdx.y * 32 + 16 * tile + m;
+  const int t0 = blockIdx.x * 16 * NTF;
+  const int nsteps = D >> 5, ET = (E + 15) >> 4;
+  const int et = blockIdx.y * 2 + tile;
+  const int e = 16 * et + m;
   const bool ev = e < E;
-  const int t = t0 + m;
-  const bool tv = t < T;
-  const int64_t plane = (int64_t)E * D;
-  const uint16_t* rb = Rs + (int64_t)(ev ? e : 0) * D + 8 * q;
-  const uint16_t* xa = x + (int64_t)(tv ? t : 0) * D + 8 * q;
-  const int nsteps = D >> 5;
+  const int64_t plane = (int64_t)ET * 16 * D;
+  // fragment-major planes: step s of tile et is the kilobyte at (et * nsteps + s) * 512
+  const uint16_t* rb = Rs + (int64_t)(et < ET ? et : ET - 1) * nsteps * 512 + 8 * l;
+  const uint16_t* xa[NTF];
+  bool tv[NTF];
+#pragma unroll
+  for (int f = 0; f < NTF; ++f) {
+    const int t = t0 + 16 * f + m;
+    tv[f] = t < T;
+    xa[f] = x + (int64_t)(tv[f] ? t : T - 1) * D + 8 * q;
+  }
   const int s0 = nsteps * kq / 4, s1 = nsteps * (kq + 1) / 4;
+  f32x4_t a0[NTF], a1[NTF], a2[NTF];
+#pragma unroll
+  for (int f = 0; f < NTF; ++f) {
+    a0[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    a1[f] = a0[f];
+    a2[f] = a0[f];
+  }
+  // software pipeline over batches of BS k-steps: the loads of batch b + 1 are issued
+  // before the matrix work of batch b; steps past s1 load the last valid step again
+  // and skip the matrix work
+  constexpr int BS = NTF == 1 ? 4 : 2;
+  u32x4_t rv[2][BS][3], xv[2][BS][NTF];
+  auto load = [&](int buf, int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      const int st = min(sb + i, s1 - 1), k0 = 32 * st;
+      rv[buf][i][0] = *(const u32x4_t*)(rb + 512 * st);
+      rv[buf][i][1] = *(const u32x4_t*)(rb + plane + 512 * st);
+      rv[buf][i][2] = *(const u32x4_t*)(rb + 2 * plane + 512 * st);
+#pragma unroll
+      for (int f = 0; f < NTF; ++f) xv[buf][i][f] = *(const u32x4_t*)(xa[f] + k0);
+    }
+  };
+  // the tile-0 waves of the first expert column store every x fragment they use,
+  // permuted, into the GEMM's copy (each fragment is a 16-byte run of 8 columns)
   const bool prep = xprep != nullptr && blockIdx.y == 0 && tile == 0;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-#pragma unroll 4
-  for (int st = s0; st < s1; ++st) {
-    const int k0 = 32 * st;
-    const u32x4_t xv = tv ? *(const u32x4_t*)(xa + k0) : zero;
-    const u32x4_t b0 = ev ? *(const u32x4_t*)(rb + k0) : zero;
-    const u32x4_t b1 = ev ? *(const u32x4_t*)(rb + plane + k0) : zero;
-    const u32x4_t b2 = ev ? *(const u32x4_t*)(rb + 2 * plane + k0) : zero;
-    a0 = mfma16x16x32(xv, b0, a0);
-    a1 = mfma16x16x32(xv, b1, a1);
-    a2 = mfma16x16x32(xv, b2, a2);
-    if (prep && tv) *(u32x4_t*)(xprep + (int64_t)t * D + k0 + 8 * q) = interleave8(xv);
+  uint16_t* xp[NTF];
+#pragma unroll
+  for (int f = 0; f < NTF; ++f) xp[f] = prep ? xprep + (int64_t)(t0 + 16 * f + m) * D + 8 * q : xprep;
+  auto mma = [&](int buf, int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+      if (sb + i < s1) {
+#pragma unroll
+        for (int f = 0; f < NTF; ++f) {
+          a0[f] = mfma16x16x32(xv[buf][i][f], rv[buf][i][0], a0[f]);
+          a1[f] = mfma16x16x32(xv[buf][i][f], rv[buf][i][1], a1[f]);
+          a2[f] = mfma16x16x32(xv[buf][i][f], rv[buf][i][2], a2[f]);
+        }
+        if (prep) {
+#pragma unroll
+          for (int f = 0; f < NTF; ++f)
+            if (tv[f]) *(u32x4_t*)(xp[f] + 32 * (sb + i)) = interleave8(xv[buf][i][f]);
+        }
+      }
+  };
+  if (s0 < s1) {
+    load(0, s0);
+    for (int sb = s0; sb < s1; sb += 2 * BS) {
+      load(1, sb + BS);
+      mma(0, sb);
+      load(0, sb + 2 * BS);
+      mma(1, sb + BS);
+    }
   }
   if (xprep && blockIdx.x == 0 && blockIdx.y == 0 && tile == 1) {
     // the zero row after the last token
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
     for (int c = kq * 64 + l; c < (D >> 3); c += 256)
       *(u32x4_t*)(xprep + (int64_t)T * D + 8 * c) = zero;
   }
-  f32x4_t acc;
+  f32x4_t acc[NTF];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = a0[i] + (a1[i] + a2[i]);
-  if (kq > 0) red[kq][tile][l] = acc;
+  for (int f = 0; f < NTF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[f][i] = a0[f][i] + (a1[f][i] + a2[f][i]);
+  if (kq > 0) {
+#pragma unroll
+    for (int f = 0; f < NTF; ++f) red[kq - 1][tile][f][l] = acc[f];
+  }
   __syncthreads();
   if (kq == 0 && ev) {
 #pragma unroll
-    for (int j = 1; j < 4; ++j) {
-      const f32x4_t o = red[j][tile][l];
+    for (int f = 0; f < NTF; ++f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += o[i];
-    }
+      for (int j = 0; j < 3; ++j) {
+        const f32x4_t o = red[j][tile][f][l];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = t0 + 4 * q + r;
-      if (tt < T) L[(int64_t)tt * E + e] = acc[r];
+        for (int i = 0; i < 4; ++i) acc[f][i] += o[i];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 16 * f + 4 * q + r;
+        if (tt < T) L[(int64_t)tt * E + e] = acc[f][r];
+      }
     }
   }
 }
 
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s) {
-  dim3 grid((T + 15) / 16, (E + 31) / 32), block(512);
-  hipLaunchKernelGGL(router_logits_kernel, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
+  dim3 block(512);
+  if (getenv("MOEQ4_ROUTER_NTF4") ? T >= 64 : T >= 2048) {
+    dim3 grid((T + 63) / 64, (E + 31) / 32);
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
+  } else {
+    dim3 grid((T + 15) / 16, (E + 31) / 32);
+    hipLaunchKernelGGL(router_logits_kernel<1>, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
+  }
 }
 
 // ---------------------------------------------------------------------------- top-k
