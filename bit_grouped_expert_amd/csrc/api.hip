@@ -38,17 +38,24 @@ moe_status check_shape(const moe_shape* s) {
 //   stream   (needs K % 128 == 0): operands streamed through an LDS ring by direct
 //            global->LDS loads; tiles of 32 rows, or 64 when groups average at
 //            least 48 rows;
-//   rows:    the first register-streaming engine, one workgroup per tile and slice.
-// The environment variable MOEQ4_GEMM=resident|stream|grouped|rows forces one (for
-// measurement and tests; an engine that cannot take the shapes falls back to grouped).
-enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM, ENG_RESIDENT };
+//   rows:    the first register-streaming engine, one workgroup per tile and slice;
+//   tiled    (K % 256 == 0, N % 256 == 0): tiles of 128 rows times blocks of 256
+//            weight rows, both operands staged through LDS per 64-K stage, the
+//            weights unpacked once per workgroup (measured no faster than resident
+//            at 8192 tokens: bound by LDS traffic; not a default).
+// The environment variable MOEQ4_GEMM=resident|stream|grouped|rows|tiled forces one
+// (for measurement and tests; an engine that cannot take the shapes falls back to
+// grouped).
+enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM, ENG_RESIDENT, ENG_TILED };
 struct GemmPlan {
   Engine eng;
   int bm;
 };
-GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok) {
+GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok,
+                   bool tiled_ok = false) {
   const int64_t g = n_groups > 0 ? n_groups : 1;
   const char* env = getenv("MOEQ4_GEMM");
+  if (env && strcmp(env, "tiled") == 0 && tiled_ok) return GemmPlan{ENG_TILED, kTiledBM};
   if (env && strcmp(env, "rows") == 0) return GemmPlan{ENG_ROWS, rows <= 64 * g ? 32 : 64};
   if (env && strcmp(env, "grouped") == 0) return GemmPlan{ENG_GROUPED, kGroupedBM};
   if (env && strcmp(env, "stream") == 0 && stream_ok)
@@ -183,12 +190,11 @@ GemmWs gemm_ws(int32_t n_groups, int32_t rows_total, int32_t a_rows, int32_t K) 
   w.tile_count = align_up((size_t)max_tiles(rows_total, n_groups, 32) * sizeof(int4));
   w.xsum = w.tile_count + kAlign;
   w.aprep = w.xsum + align_up((size_t)a_rows * (size_t)(K / 64) * 4);
-  w.xc = w.aprep;
-  w.total = w.aprep;
-  if (K % 128 == 0) {  // the streamed engine's prepared copy of A
-    w.xc = w.aprep + align_up(((size_t)a_rows + 1) * (size_t)K * 2);
+  // the prepared copy of A (resident, tiled and streamed engines)
+  w.xc = w.aprep + align_up(((size_t)a_rows + 1) * (size_t)K * 2);
+  w.total = w.xc;
+  if (K % 128 == 0)  // the streamed engine's per-stage row sums
     w.total = w.xc + align_up(((size_t)a_rows + 1) * (size_t)(K / 128) * 16);
-  }
   return w;
 }
 }  // namespace
@@ -294,12 +300,34 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
   const bool resident_ok =
       a_rows >= 1 &&
       resident_plan(N, K, epilogue == 1, max_tiles(rows_total, n_groups, kResidentBM), n_cu, &rplan);
-  const GemmPlan plan =
-      plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows), resident_ok);
+  const GemmPlan plan = plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows), resident_ok,
+                                  tiled_supported(N, K, epilogue == 1, a_rows));
   int4* tiles = at<int4>(ws, gw.tiles);
   int32_t* tile_count = at<int32_t>(ws, gw.tile_count);
   float* xsum = at<float>(ws, gw.xsum);
   launch_build_tiles(offsets, n_groups, rows_total, plan.bm, tiles, tile_count, stream);
+  if (plan.eng == ENG_TILED) {
+    // prepared copy of A (column order 0,4,1,5,... per run of 8, one zero row after the last)
+    uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
+    launch_prep(A, a_rows, K, aprep, nullptr, stream);
+    TiledParams tp;
+    memset(&tp, 0, sizeof(tp));
+    tp.A = aprep;
+    tp.a_row_index = a_row_index;
+    tp.a_rows = a_rows;
+    tp.main = Q4Ptrs{W.q, W.scale, W.bias};
+    tp.n_main = n_groups;
+    tp.last = tp.main;
+    tp.N = N;
+    tp.K = K;
+    tp.C = C;
+    tp.ldc = epilogue == 1 ? N / 2 : N;
+    tp.c_perm = 0;
+    tp.tiles = tiles;
+    tp.tile_count = tile_count;
+    launch_tiled(tp, epilogue == 1, max_tiles(rows_total, n_groups, kTiledBM), stream);
+    return launch_status();
+  }
   if (plan.eng == ENG_RESIDENT) {
     // prepared copy of A (column order 0,4,1,5,... per run of 8, one zero row after the last)
     uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
@@ -426,14 +454,17 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   ResidentPlan rp_up, rp_down;
   const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &rp_up) &&
                            resident_plan(D, F, false, rbound, n_cu, &rp_down);
-  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok);
+  const bool tiled_ok = tiled_supported(2 * F, D, true, T) && tiled_supported(D, F, false, rows);
+  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok, tiled_ok);
   // routing
   mark(0);
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
   launch_router_split(router_w, Rs, E, D, stream);
   launch_router_logits(x, Rs, logits, T, D, E,
-                       plan.eng == ENG_RESIDENT ? at<uint16_t>(ws, L.xprep) : nullptr, stream);
+                       plan.eng == ENG_RESIDENT || plan.eng == ENG_TILED ? at<uint16_t>(ws, L.xprep)
+                                                                         : nullptr,
+                       stream);
   launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
   mark(1);
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
@@ -448,6 +479,47 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   if (plan.eng == ENG_STREAM) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), at<float4>(ws, L.xc_x), stream);
   else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
+
+  if (plan.eng == ENG_TILED) {
+    // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act, stored
+    // in the prepared column order so that the down GEMM reads it as is
+    TiledParams tp;
+    memset(&tp, 0, sizeof(tp));
+    tp.A = at<uint16_t>(ws, L.xprep);
+    tp.a_row_index = sorted_tok;
+    tp.a_rows = T;
+    tp.main = Q4Ptrs{experts->gate_up.q, experts->gate_up.scale, experts->gate_up.bias};
+    tp.n_main = E;
+    tp.last = has_shared ? Q4Ptrs{shared->gate_up.q, shared->gate_up.scale, shared->gate_up.bias}
+                         : tp.main;
+    tp.N = 2 * F;
+    tp.K = D;
+    tp.C = act;
+    tp.ldc = F;
+    tp.c_perm = 1;
+    tp.tiles = tiles;
+    tp.tile_count = tile_count;
+    const int64_t tbound = max_tiles(rows, n_groups, kTiledBM);
+    launch_tiled(tp, true, tbound, stream);
+    mark(3);
+    // down: act rows in order -> y [rows, D]
+    tp.A = act;
+    tp.a_row_index = nullptr;
+    tp.a_rows = rows;
+    tp.main = Q4Ptrs{experts->down.q, experts->down.scale, experts->down.bias};
+    tp.last = has_shared ? Q4Ptrs{shared->down.q, shared->down.scale, shared->down.bias} : tp.main;
+    tp.N = D;
+    tp.K = F;
+    tp.C = y;
+    tp.ldc = D;
+    tp.c_perm = 0;
+    launch_tiled(tp, false, tbound, stream);
+    mark(4);
+    launch_combine(y, (int64_t)T * k, slot_row, wts,
+                   has_shared ? y + (int64_t)T * k * D : nullptr, out, T, D, k, stream);
+    mark(5);
+    return launch_status();
+  }
 
   if (plan.eng == ENG_RESIDENT) {
     // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act, stored

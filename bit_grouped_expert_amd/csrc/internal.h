@@ -142,6 +142,31 @@ struct ResidentPlan {
 bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, ResidentPlan* out);
 void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hipStream_t s);
 
+// Tiled engine (grouped_tiled.hip), for large groups: one workgroup per tile of up to
+// 128 rows (tile map built with bm = kTiledBM), walking every block of 256 weight rows
+// through LDS-staged 64-K stages.  A is the prepared copy (each run of 8 columns stored
+// in the order 0,4,1,5,2,6,3,7) and row a_rows of A must be readable and zero where a
+// row index can fall outside [0, a_rows).  Needs K % 256 == 0, N % 256 == 0 (SwiGLU:
+// N = 2F with F % 128 == 0) and a_rows >= 1; C rows are written with 8-byte stores
+// (ldc % 4 == 0).  With SwiGLU and c_perm set, C is stored in the prepared column order.
+constexpr int kTiledBM = 128;
+struct TiledParams {
+  const uint16_t* A;          // prepared bf16 [a_rows (+1), K]
+  const int32_t* a_row_index; // nullable: identity
+  int32_t a_rows;
+  Q4Ptrs main;
+  int32_t n_main;
+  Q4Ptrs last;
+  int32_t N, K;
+  uint16_t* C;
+  int32_t ldc;
+  int32_t c_perm;
+  const int4* tiles;
+  const int32_t* tile_count;
+};
+bool tiled_supported(int N, int K, bool swiglu, int a_rows);
+void launch_tiled(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
                     const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);

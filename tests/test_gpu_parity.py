@@ -35,7 +35,7 @@ def torch_cuda():
     return torch
 
 
-ENGINES = ["rows", "grouped", "stream", "resident"]
+ENGINES = ["rows", "grouped", "stream", "resident", "tiled"]
 
 
 @pytest.fixture
@@ -91,6 +91,9 @@ GEMM_INT_CASES = [
     ([5, 0, 70, 3, 16], 512, 1536, False),          # halves of three stages, no prefetch
     ([1, 31, 32, 33], 768, 256, False),             # one stage over the whole K
     ([40, 2, 0, 27], 256, 512, True),               # whole K per wavefront, two stages
+    ([257, 0, 600, 1, 130], 256, 256, True),        # 128-row tiles: full, 1-row, ragged
+    ([513, 16, 255], 512, 512, False),              # two weight blocks of 256 rows
+    ([300, 129], 768, 768, True),                   # three weight blocks, twelve 64-K stages
 ]
 
 
@@ -362,7 +365,7 @@ def test_layer_forward_parity_full(torch_cuda, name):
     _layer_full_check(torch_cuda, cfg)
 
 
-@pytest.mark.parametrize("engine", ["rows", "grouped", "stream"], indirect=True)
+@pytest.mark.parametrize("engine", ["rows", "grouped", "stream", "tiled"], indirect=True)
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_layer_forward_parity_full_rows(torch_cuda, name, engine):
     """The same layers through the engines the default does not pick for them."""
