@@ -152,20 +152,39 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   int4* segt = (int4*)(smem + seg_off(K));
   int* idxt = (int*)(smem + idx_off(K));
 
-  // ---- this workgroup's range of (tile, chunk) pairs
+  // ---- this workgroup's (tile, chunk) pairs.  With few tiles per workgroup: an equal
+  // contiguous range of the pairs, the workgroups of one XCD on adjacent ranges.  With
+  // at least eight tiles per workgroup: XCD x takes the x-th eighth of the tiles and
+  // deals them round robin to its workgroups, each taking whole tiles, so that at any
+  // time an XCD works on a few consecutive groups whose weights its L2 shares.
   const int cnt = *p.tile_count;
-  const int G = gridDim.x;
-  const int rank = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int64_t total = (int64_t)cnt * NCH;
-  const int c_begin = (int)(total * rank / G), c_end = (int)(total * (rank + 1) / G);
+  const int G = gridDim.x, WX = G >> 3;  // workgroups per XCD
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const bool dealt = cnt >= 8 * G;
+  int c_begin, c_end, t_first, nseg, t_lo = 0;
+  if (dealt) {
+    t_lo = (int)((int64_t)cnt * xcd / 8);
+    const int t_hi = (int)((int64_t)cnt * (xcd + 1) / 8);
+    nseg = t_lo + jw < t_hi ? (t_hi - t_lo - jw + WX - 1) / WX : 0;
+    c_begin = 0;
+    c_end = nseg * NCH;
+    t_first = 0;
+  } else {
+    const int rank = xcd * WX + jw;
+    const int64_t total = (int64_t)cnt * NCH;
+    c_begin = (int)(total * rank / G);
+    c_end = (int)(total * (rank + 1) / G);
+    t_first = c_begin / NCH;
+    nseg = c_begin < c_end ? (c_end - 1) / NCH - t_first + 1 : 0;
+  }
   if (c_begin >= c_end) return;  // uniform, before any barrier
-  const int t_first = c_begin / NCH;
-  const int nseg = (c_end - 1) / NCH - t_first + 1;
   if (nseg > SEG_CAP) return;    // excluded by the host; never write past the table
+  // segment k's tile: the k-th of the range, or the k-th dealt to this workgroup
+  auto tile_of = [&](int k) -> int { return dealt ? t_lo + jw + WX * k : t_first + k; };
   // tiles and activation row indices of every segment, before any weight load
   for (int e = tid; e < nseg * 32; e += 512) {
     const int k = e >> 5, rr = e & 31;
-    const int4 t = p.tiles[t_first + k];
+    const int4 t = p.tiles[tile_of(k)];
     if (rr == 0) segt[k] = t;
     const int row = t.y + (rr < t.z ? rr : t.z - 1);
     int a = p.a_row_index ? p.a_row_index[row] : row;
@@ -540,6 +559,10 @@ bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, R
   const int64_t per_wg = (chunks + grid - 1) / grid;
   const int64_t segs = (per_wg - 1) / NCH + 2;
   if (segs > SEG_CAP) return false;
+  // tiles dealt round robin (at least eight per workgroup): an XCD's share over its
+  // workgroups
+  const int64_t tiles = n_tiles_bound > 0 ? n_tiles_bound : 1;
+  if (((tiles + 7) / 8 + grid / 8 - 1) / (grid / 8) > SEG_CAP) return false;
   if (out) {
     out->ksplit = S;
     out->stages = nst;

@@ -20,8 +20,6 @@
 // fp64) and the top k of those, by fp64 logit, are chosen.  Any expert outside
 // that set has a true logit below k+1 candidates' as long as the fp32 error is
 // under tau/2, so the selection equals the exact (fp64) top-k.
-#include <cstdlib>
-
 #include "common.h"
 #include "internal.h"
 
@@ -217,7 +215,7 @@ __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __re
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s) {
   dim3 block(512);
-  if (getenv("MOEQ4_ROUTER_NTF4") ? T >= 64 : T >= 2048) {
+  if (T >= 2048) {
     dim3 grid((T + 63) / 64, (E + 31) / 32);
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
   } else {
