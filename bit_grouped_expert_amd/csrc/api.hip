@@ -201,7 +201,8 @@ GemmWs gemm_ws(int32_t n_groups, int32_t rows_total, int32_t a_rows, int32_t K) 
 
 size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total, int32_t a_rows,
                                            int32_t K) {
-  if (n_groups < 1 || rows_total < 0 || a_rows < 0 || K <= 0 || K % 64) return 0;
+  if (n_groups < 1 || n_groups > kMaxTileGroups || rows_total < 0 || a_rows < 0 || K <= 0 || K % 64)
+    return 0;
   return gemm_ws(n_groups, rows_total, a_rows, K).total;
 }
 
@@ -279,8 +280,8 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
                                const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
                                const int32_t* offsets, moe_q4 W, int32_t epilogue, uint16_t* C,
                                void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (n_groups < 1 || rows_total < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 ||
-      (epilogue != 0 && epilogue != 1))
+  if (n_groups < 1 || n_groups > kMaxTileGroups || rows_total < 0 || a_rows < 0 || N <= 0 ||
+      K <= 0 || N % 64 || K % 64 || (epilogue != 0 && epilogue != 1))
     return MOE_ERR_SHAPE;
   const int64_t widest = N > K ? N : K;
   if ((int64_t)rows_total * widest >= ((int64_t)1 << 31) ||

@@ -52,6 +52,7 @@ struct GemmParams {
   int32_t xsum_out_ld;
 };
 
+constexpr int kMaxTileGroups = 1025;  // groups of a tile map: 1024 routed experts + the shared one
 inline int64_t max_tiles(int64_t rows_total, int n_groups, int bm) {
   return (rows_total + bm - 1) / bm + n_groups;
 }

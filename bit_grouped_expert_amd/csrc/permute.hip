@@ -153,39 +153,62 @@ void launch_scatter(const int32_t* idx, int T, int k, int E, const int32_t* chun
 }
 
 // ---------------------------------------------------------------------------- tile map
-// One workgroup of 1024 threads: tiles of at most `bm` rows over every group,
-// group by group, as (group, first row, rows, 0).  Offsets are clamped into
-// [0, rows_total] so that no tile leaves C, and at most `cap` tiles are written
-// (cap = the bound the grid was sized with), so malformed offsets cannot
-// overrun the tile array.
-// Tile map over group boundaries offs[0..n_groups] (read from global memory or LDS);
-// every thread of a 1024-thread workgroup calls it.
+// Tiles of at most `bm` rows over every group, group by group, as (group, first row,
+// rows, 0).  Offsets are clamped into [0, rows_total] so that no tile leaves C, and at
+// most `cap` tiles are written (cap = the bound the grid was sized with), so malformed
+// offsets cannot overrun the tile array.  Every thread of a 1024-thread workgroup
+// calls it; `tab` is LDS scratch of at least 3 * (n_groups + 1) ints.  A scan gives
+// each group its first tile, then tile t is written by thread t % 1024, which finds its
+// group by binary search over the first tiles (consecutive threads write consecutive
+// tiles).
 __device__ void write_tiles(const int32_t* offs, int n_groups, int rows_total, int bm,
-                            int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
+                            int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count,
+                            int* tab) {
+  int* first = tab;                   // [n_groups + 1]
+  int* glo = tab + n_groups + 1;      // [n_groups]
+  int* ghi = glo + n_groups;          // [n_groups]
+  __syncthreads();  // the caller may have used the scratch
   int running = 0;
   for (int g0 = 0; g0 < n_groups; g0 += 1024) {
     const int g = g0 + threadIdx.x;
-    int lo = 0, n = 0;
+    int lo = 0, hi = 0;
     if (g < n_groups) {
       lo = min(max(offs[g], 0), rows_total);
-      int hi = min(max(offs[g + 1], lo), rows_total);
-      n = hi - lo;
+      hi = min(max(offs[g + 1], lo), rows_total);
     }
-    const int nt = (n + bm - 1) / bm;
+    const int nt = (hi - lo + bm - 1) / bm;
     int total;
-    const int first = running + block_exclusive_scan_1024(nt, &total);
-    for (int i = 0; i < nt && first + i < cap; ++i)
-      tiles[first + i] = make_int4(g, lo + i * bm, min(bm, n - i * bm), 0);
+    const int f = running + block_exclusive_scan_1024(nt, &total);
+    if (g < n_groups) {
+      first[g] = f;
+      glo[g] = lo;
+      ghi[g] = hi;
+    }
     running += total;
   }
-  if (threadIdx.x == 0) *tile_count = min(running, cap);
+  if (threadIdx.x == 0) first[n_groups] = running;
+  __syncthreads();
+  const int ntot = min(running, cap);
+  for (int t = threadIdx.x; t < ntot; t += 1024) {
+    // the last group whose first tile is <= t (empty groups share their successor's)
+    int a = 0, b = n_groups - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (first[mid] <= t) a = mid;
+      else b = mid - 1;
+    }
+    const int r0 = glo[a] + (t - first[a]) * bm;
+    tiles[t] = make_int4(a, r0, min(bm, ghi[a] - r0), 0);
+  }
+  if (threadIdx.x == 0) *tile_count = ntot;
 }
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int n_groups, int rows_total, int bm,
                                                            int4* __restrict__ tiles, int cap,
                                                            int32_t* __restrict__ tile_count) {
-  write_tiles(offsets, n_groups, rows_total, bm, tiles, cap, tile_count);
+  __shared__ int tab[3 * (kMaxTileGroups + 1)];
+  write_tiles(offsets, n_groups, rows_total, bm, tiles, cap, tile_count, tab);
 }
 
 void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
@@ -260,7 +283,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   }
   const int n_groups = E + (shared_rows >= 0 ? 1 : 0);
   const int rows_total = T * k + (shared_rows >= 0 ? shared_rows : 0);
-  write_tiles(offs, n_groups, rows_total, bm, tiles, cap, tile_count);
+  // the masks are no longer needed: their space (16 E words) holds the tile scratch
+  write_tiles(offs, n_groups, rows_total, bm, tiles, cap, tile_count, (int*)masks);
 }
 
 constexpr size_t small_lds(int E) {

@@ -15,11 +15,12 @@
 // Selection.  One wavefront per token ranks the logits by a 64-bit key
 // (order-preserving float bits, then the complemented expert id so equal logits
 // rank the lower id higher) and extracts the k+1 best.  If the k-th and (k+1)-th
-// fp32 logits are closer than `tau`, every expert whose fp32 logit is at least
-// L_(k+1) - tau is rescored exactly in fp64 (bf16 x fp32 products are exact in
-// fp64) and the top k of those, by fp64 logit, are chosen.  Any expert outside
-// that set has a true logit below k+1 candidates' as long as the fp32 error is
-// under tau/2, so the selection equals the exact (fp64) top-k.
+// fp32 logits are closer than `tau`, the experts at least tau above L_(k+1) keep
+// their places, and every expert within tau of L_(k+1) is rescored exactly in fp64
+// (bf16 x fp32 products are exact in fp64); the best of those, by fp64 logit, fill
+// the remaining places.  As long as the fp32 error is under tau/2 the experts above
+// are in the exact top k and those below are not, so the selection equals the
+// exact (fp64) top-k; the places filled by rescoring are in exact order.
 #include "common.h"
 #include "internal.h"
 
@@ -297,30 +298,71 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
     const float vk = __shfl(my_v, k - 1);
     const float vk1 = __shfl(my_v, k);
     if (vk - vk1 < tau) {
-      // exact rescoring of every expert within tau below the (k+1)-th logit
-      const float thr = vk1 - tau;
+      // With an fp32 error below tau / 2: an expert whose fp32 logit is at least
+      // L_(k+1) + tau is in the exact top k (it is among the fp32 top k, and only those
+      // could beat it), one below L_(k+1) - tau is not (the k + 1 fp32 best beat it).
+      // The first kind keep their places (a prefix of the ranking); the experts in
+      // between are rescored exactly in fp64 and fill the remaining places.  Four
+      // candidates per pass over x: lane d sums d, d + 64, ... in order (several steps
+      // of loads in flight), then a fixed butterfly adds the lanes.
+      const float thr_lo = vk1 - tau, thr_hi = vk1 + tau;
+      const int n_sure = __popcll(__ballot(lane < k && my_v >= thr_hi));
       double exact[MAXC];
       bool cand[MAXC];
       const uint16_t* xt = x + (int64_t)t * D;
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = c * 64 + lane;
-        cand[c] = e < E && val[c] >= thr;
+        cand[c] = e < E && val[c] >= thr_lo && !(val[c] >= thr_hi);
         exact[c] = 0.0;
+      }
+      int ce[4] = {0, 0, 0, 0}, nb = 0;  // expert ids of the pending batch (uniform)
+      auto flush = [&]() __attribute__((always_inline)) {
+        const float* Rr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Rr[j] = R + (int64_t)(j < nb ? ce[j] : ce[0]) * D;
+        double sj[4] = {0.0, 0.0, 0.0, 0.0};
+        constexpr int UN = MAXC >= 16 ? 2 : 8;  // steps in flight (registers permitting)
+        for (int d0 = 0; d0 < D; d0 += 64 * UN) {
+          float xv[UN], rv[UN][4];
+#pragma unroll
+          for (int u = 0; u < UN; ++u) {
+            const int d = min(d0 + 64 * u + lane, D - 1);
+            xv[u] = d0 + 64 * u + lane < D ? bf16lo_to_f32(xt[d]) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rv[u][j] = Rr[j][d];
+          }
+#pragma unroll
+          for (int u = 0; u < UN; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sj[j] += (double)xv[u] * (double)rv[u][j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double sum = wave_sum_f64(sj[j]);
+          if (j < nb && (ce[j] & 63) == lane) {
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c)
+              if (c == (ce[j] >> 6)) exact[c] = sum;
+          }
+        }
+        nb = 0;
+      };
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
         uint64_t mask = __ballot(cand[c]);
         while (mask) {
           const int b = __builtin_ctzll(mask);
           mask &= mask - 1;
-          const float* Re = R + (int64_t)(c * 64 + b) * D;
-          double s = 0.0;
-          for (int d = lane; d < D; d += 64)
-            s += (double)bf16lo_to_f32(xt[d]) * (double)Re[d];
-          s = wave_sum_f64(s);
-          if (lane == b) exact[c] = s;
+          // ce[nb] = c * 64 + b, without a dynamically indexed array
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ce[j] = j == nb ? c * 64 + b : ce[j];
+          if (++nb == 4) flush();
         }
       }
-      // top-k of the candidates by (fp64 logit desc, expert id asc)
-      for (int j = 0; j < k; ++j) {
+      if (nb > 0) flush();
+      // the remaining places from the candidates by (fp64 logit desc, expert id asc)
+      for (int j = n_sure; j < k; ++j) {
         Cand best{-__builtin_inf(), 0x7FFFFFFF};
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {

@@ -152,7 +152,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
  *   H[r] = A[row(r)] W_g^T   (fp32),  row(r) = a_row_index ? a_row_index[r] : r
  *   epilogue 0: C[r][n] = bf16(H[r][n]),            C is [rows_total, N]
  *   epilogue 1: C[r][f] = bf16(silu(H[r][f]) * H[r][N/2 + f]), C is [rows_total, N/2]
- *   n_groups   >= 1;  N % 64 == 0;  K % 64 == 0;  rows_total >= 0
+ *   1 <= n_groups <= 1025;  N % 64 == 0;  K % 64 == 0;  rows_total >= 0
  *   A          bf16 [a_rows, K]; rows whose index is outside [0, a_rows) read as zero
  *   offsets    int32 [n_groups + 1] on the device, non-decreasing from 0;
  *              values are clamped to [0, rows_total]; C rows outside every
