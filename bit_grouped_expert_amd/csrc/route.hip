@@ -241,6 +241,42 @@ __device__ __forceinline__ uint64_t ordered_bits64(double v) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Wavefront reductions with DPP, the result on every lane: within each row of 16 lanes
+// (quad swaps, then rotations by 4 and 8), then the row results carried to lane 63 by
+// the row broadcasts of lane 15 and lane 31, read back as a scalar.  Lanes a DPP step
+// does not update contribute the identity.  The order of the additions is fixed.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v, uint32_t identity, Op op) {
+  const int id = (int)identity;
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  return __uint_as_float(wave_reduce_dpp(__float_as_uint(v), 0xFF800000u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return __uint_as_float(wave_reduce_dpp(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+// the largest 64-bit key of the wavefront: the largest high word, then the largest
+// low word among the lanes that hold it
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // (value, expert) pair order: larger value first, then lower expert id.
 struct Cand {
   double v;
@@ -280,7 +316,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
     uint64_t best = 0;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_u64(best);
+    best = wave_max_key(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
     const float v = unordered_bits((uint32_t)(best >> 32));
     if (lane == j) {
@@ -295,8 +331,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
   }
 
   if (k < E) {
-    const float vk = __shfl(my_v, k - 1);
-    const float vk1 = __shfl(my_v, k);
+    const float vk = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_v), k - 1));
+    const float vk1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_v), k));
     if (vk - vk1 < tau) {
       // With an fp32 error below tau / 2: an expert whose fp32 logit is at least
       // L_(k+1) + tau is in the exact top k (it is among the fp32 top k, and only those
@@ -392,13 +428,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
 
   // softmax over the k selected fp32 logits
   const bool mine = lane < k;
-  float mx = mine ? my_v : -__builtin_inff();
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+  const float mx = wave_max_f32(mine ? my_v : -__builtin_inff());
   const float z = mine ? __expf(my_v - mx) : 0.f;
-  float sum = z;
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk);
+  const float sum = wave_sum_f32(z);
   if (mine) {
     idx_out[(int64_t)t * k + lane] = my_e;
     w_out[(int64_t)t * k + lane] = z / sum;
