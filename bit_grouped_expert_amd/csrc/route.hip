@@ -213,10 +213,124 @@ __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Many tokens (T >= 2048, D % 256 == 0): workgroup tile of 64 tokens x 128 experts, its
+// eight wavefronts one 16-expert tile each over the whole K, so that R (three planes)
+// is read T / 64 times and x E / 128 times.  The tile's x rows go through LDS in chunks
+// of 256 k: every thread loads 16-byte pieces of whole 512-byte row runs (line-whole,
+// rows read once per workgroup) one chunk ahead, and writes them into the other buffer
+// in fragment order.  A piece (fragment f, 32-k step s, quarter q, row m) sits at
+// (8 f + s) * 1088 + (17 q + m) * 16 bytes: a wavefront's reads are conflict-free and
+// its writes of one row's pieces at most two-way.  Each wavefront's R fragments for a
+// step are loaded one chunk (eight steps) ahead.  The workgroups of the first expert
+// column also write the prepared copy of x from the pieces they load.
+constexpr int kWideTok = 64, kWideExp = 128, kWideKC = 256;
+constexpr int kWideBlock = 1088;  // bytes per (fragment, step) block, padded
+__global__ __launch_bounds__(512) void router_logits_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Rs, float* __restrict__ L, int T,
+    int D, int E, uint16_t* __restrict__ xprep) {
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][4 * 8 * kWideBlock];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int m = l & 15, q = l >> 4;
+  const int t0 = blockIdx.x * kWideTok;
+  const int nsteps = D >> 5, ET = (E + 15) >> 4, nch = D / kWideKC;
+  const int et = blockIdx.y * 8 + wave;
+  const int e = 16 * et + m;
+  const bool ev = e < E;
+  const int64_t plane = (int64_t)ET * 16 * D;
+  const uint16_t* rb = Rs + (int64_t)(et < ET ? et : ET - 1) * nsteps * 512 + 8 * l;
+  // this thread's x pieces: rows (tid / 32) + 16 i, piece c = tid % 32 of each 512-byte run
+  const int pc = tid & 31, pr = tid >> 5;
+  const uint16_t* xsrc[4];
+  bool tv[4];
+  uint32_t xdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + pr + 16 * i;
+    tv[i] = t < T;
+    xsrc[i] = x + (int64_t)(tv[i] ? t : T - 1) * D + 8 * pc;
+    xdst[i] = (uint32_t)((8 * i + (pc >> 2)) * kWideBlock + (17 * (pc & 3) + pr) * 16);
+  }
+  const bool prep = xprep != nullptr && blockIdx.y == 0;
+  auto load_x = [&](u32x4_t* xr, int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = *(const u32x4_t*)(xsrc[i] + ch * kWideKC);
+  };
+  auto store_x = [&](const u32x4_t* xr, int ch, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)(&xs[buf][xdst[i]]) = xr[i];
+    if (prep) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tv[i])
+          *(u32x4_t*)(xprep + (int64_t)(t0 + pr + 16 * i) * D + ch * kWideKC + 8 * pc) =
+              interleave8(xr[i]);
+    }
+  };
+  auto load_r = [&](u32x4_t* rv, int gs) __attribute__((always_inline)) {
+    rv[0] = *(const u32x4_t*)(rb + 512 * gs);
+    rv[1] = *(const u32x4_t*)(rb + plane + 512 * gs);
+    rv[2] = *(const u32x4_t*)(rb + 2 * plane + 512 * gs);
+  };
+  f32x4_t a0[4], a1[4], a2[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    a0[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    a1[f] = a0[f];
+    a2[f] = a0[f];
+  }
+  u32x4_t rv[8][3], xr[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) load_r(rv[s], s);
+  load_x(xr, 0);
+  store_x(xr, 0, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    const bool more = ch + 1 < nch;
+    const int chn = more ? ch + 1 : ch;  // the last chunk loads itself again
+    load_x(xr, chn);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4_t xa[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        xa[f] = *(const u32x4_t*)(&xs[buf][(8 * f + s) * kWideBlock + (17 * q + m) * 16]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a0[f] = mfma16x16x32(xa[f], rv[s][0], a0[f]);
+        a1[f] = mfma16x16x32(xa[f], rv[s][1], a1[f]);
+        a2[f] = mfma16x16x32(xa[f], rv[s][2], a2[f]);
+      }
+      load_r(rv[s], 8 * chn + s);
+    }
+    if (more) {
+      store_x(xr, chn, buf ^ 1);
+      __syncthreads();
+    }
+  }
+  if (xprep && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) {
+    // the zero row after the last token
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int c = l; c < (D >> 3); c += 64) *(u32x4_t*)(xprep + (int64_t)T * D + 8 * c) = zero;
+  }
+  if (ev) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 16 * f + 4 * q + r;
+        if (tt < T) L[(int64_t)tt * E + e] = a0[f][r] + (a1[f][r] + a2[f][r]);
+      }
+  }
+}
+
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s) {
   dim3 block(512);
-  if (T >= 2048) {
+  if (T >= 2048 && D % kWideKC == 0) {
+    dim3 grid((T + kWideTok - 1) / kWideTok, (E + kWideExp - 1) / kWideExp);
+    hipLaunchKernelGGL(router_logits_wide_kernel, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
+  } else if (T >= 2048) {
     dim3 grid((T + 63) / 64, (E + 31) / 32);
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, block, 0, s, x, Rs, L, T, D, E, xprep);
   } else {
