@@ -53,7 +53,7 @@ namespace moeq4 {
 namespace {
 
 constexpr int KS = 256;            // K per stage: four scale groups (two halves of 128)
-constexpr int SEG_CAP = 32;        // most tiles one workgroup may touch (host-checked)
+constexpr int SEG_CAP = 48;        // most tiles one workgroup may touch (host-checked)
 constexpr int PART_BYTES = 16384;  // partial sums / output staging
 constexpr uint32_t kMagic = 0x43004300u;
 constexpr uint32_t kNib = 0x000F000Fu;
