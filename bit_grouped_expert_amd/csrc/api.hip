@@ -43,18 +43,22 @@ moe_status check_shape(const moe_shape* s) {
 //            weight rows, both operands staged through LDS per 64-K stage, the
 //            weights unpacked once per workgroup (measured no faster than resident
 //            at 8192 tokens: bound by LDS traffic; not a default).
-// The environment variable MOEQ4_GEMM=resident|stream|grouped|rows|tiled forces one
+//   wide     (K % 256 == 0, K <= 2048, N % 256 == 0): tiles of 128 rows, weights
+//            streamed into VGPRs, each packed word feeding eight row fragments, the
+//            activations through two LDS stage buffers.
+// The environment variable MOEQ4_GEMM=resident|stream|grouped|rows|tiled|wide forces one
 // (for measurement and tests; an engine that cannot take the shapes falls back to
 // grouped).
-enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM, ENG_RESIDENT, ENG_TILED };
+enum Engine { ENG_ROWS, ENG_GROUPED, ENG_STREAM, ENG_RESIDENT, ENG_TILED, ENG_WIDE };
 struct GemmPlan {
   Engine eng;
   int bm;
 };
 GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok,
-                   bool tiled_ok = false) {
+                   bool tiled_ok = false, bool wide_ok = false) {
   const int64_t g = n_groups > 0 ? n_groups : 1;
   const char* env = getenv("MOEQ4_GEMM");
+  if (env && strcmp(env, "wide") == 0 && wide_ok) return GemmPlan{ENG_WIDE, kWideBM};
   if (env && strcmp(env, "tiled") == 0 && tiled_ok) return GemmPlan{ENG_TILED, kTiledBM};
   if (env && strcmp(env, "rows") == 0) return GemmPlan{ENG_ROWS, rows <= 64 * g ? 32 : 64};
   if (env && strcmp(env, "grouped") == 0) return GemmPlan{ENG_GROUPED, kGroupedBM};
@@ -302,12 +306,13 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
       a_rows >= 1 &&
       resident_plan(N, K, epilogue == 1, max_tiles(rows_total, n_groups, kResidentBM), n_cu, &rplan);
   const GemmPlan plan = plan_gemm(rows_total, n_groups, stream_supported(N, K, a_rows), resident_ok,
-                                  tiled_supported(N, K, epilogue == 1, a_rows));
+                                  tiled_supported(N, K, epilogue == 1, a_rows),
+                                  wide_supported(N, K, epilogue == 1, a_rows));
   int4* tiles = at<int4>(ws, gw.tiles);
   int32_t* tile_count = at<int32_t>(ws, gw.tile_count);
   float* xsum = at<float>(ws, gw.xsum);
   launch_build_tiles(offsets, n_groups, rows_total, plan.bm, tiles, tile_count, stream);
-  if (plan.eng == ENG_TILED) {
+  if (plan.eng == ENG_TILED || plan.eng == ENG_WIDE) {
     // prepared copy of A (column order 0,4,1,5,... per run of 8, one zero row after the last)
     uint16_t* aprep = at<uint16_t>(ws, gw.aprep);
     launch_prep(A, a_rows, K, aprep, nullptr, stream);
@@ -326,7 +331,8 @@ moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, 
     tp.c_perm = 0;
     tp.tiles = tiles;
     tp.tile_count = tile_count;
-    launch_tiled(tp, epilogue == 1, max_tiles(rows_total, n_groups, kTiledBM), stream);
+    if (plan.eng == ENG_WIDE) launch_wide(tp, epilogue == 1, max_tiles(rows_total, n_groups, kWideBM), stream);
+    else launch_tiled(tp, epilogue == 1, max_tiles(rows_total, n_groups, kTiledBM), stream);
     return launch_status();
   }
   if (plan.eng == ENG_RESIDENT) {
@@ -456,15 +462,17 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &rp_up) &&
                            resident_plan(D, F, false, rbound, n_cu, &rp_down);
   const bool tiled_ok = tiled_supported(2 * F, D, true, T) && tiled_supported(D, F, false, rows);
-  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok, tiled_ok);
+  const bool wide_ok = wide_supported(2 * F, D, true, T) && wide_supported(D, F, false, rows);
+  const GemmPlan plan = plan_gemm(rows, n_groups, layer_stream_ok(shape), resident_ok, tiled_ok, wide_ok);
   // routing
   mark(0);
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
   launch_router_split(router_w, Rs, E, D, stream);
   launch_router_logits(x, Rs, logits, T, D, E,
-                       plan.eng == ENG_RESIDENT || plan.eng == ENG_TILED ? at<uint16_t>(ws, L.xprep)
-                                                                         : nullptr,
+                       plan.eng == ENG_RESIDENT || plan.eng == ENG_TILED || plan.eng == ENG_WIDE
+                           ? at<uint16_t>(ws, L.xprep)
+                           : nullptr,
                        stream);
   launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
   mark(1);
@@ -481,7 +489,7 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);
   mark(2);
 
-  if (plan.eng == ENG_TILED) {
+  if (plan.eng == ENG_TILED || plan.eng == ENG_WIDE) {
     // gate_up + SwiGLU over the prepared x rows gathered through sorted_tok -> act, stored
     // in the prepared column order so that the down GEMM reads it as is
     TiledParams tp;
@@ -500,8 +508,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
     tp.c_perm = 1;
     tp.tiles = tiles;
     tp.tile_count = tile_count;
-    const int64_t tbound = max_tiles(rows, n_groups, kTiledBM);
-    launch_tiled(tp, true, tbound, stream);
+    const bool wide = plan.eng == ENG_WIDE;
+    const int64_t tbound = max_tiles(rows, n_groups, wide ? kWideBM : kTiledBM);
+    if (wide) launch_wide(tp, true, tbound, stream);
+    else launch_tiled(tp, true, tbound, stream);
     mark(3);
     // down: act rows in order -> y [rows, D]
     tp.A = act;
@@ -514,7 +524,8 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
     tp.C = y;
     tp.ldc = D;
     tp.c_perm = 0;
-    launch_tiled(tp, false, tbound, stream);
+    if (wide) launch_wide(tp, false, tbound, stream);
+    else launch_tiled(tp, false, tbound, stream);
     mark(4);
     launch_combine(y, (int64_t)T * k, slot_row, wts,
                    has_shared ? y + (int64_t)T * k * D : nullptr, out, T, D, k, stream);

@@ -48,6 +48,7 @@
 // contiguous kilobyte.
 #include "common.h"
 #include "internal.h"
+#include "q4_stream.h"
 
 namespace moeq4 {
 
@@ -64,36 +65,6 @@ constexpr int OFF_SB = OFF_B + 2 * B_STAGE;       // (s, b) bf16 pairs [2][4][TN
 constexpr int OFF_X = OFF_SB + 2 * 4 * TN * 4;    // X per token, fp32 [RING][TM]
 constexpr int LDS_BYTES = OFF_X + RING * TM * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-constexpr uint32_t kMagic = 0x43004300u;
-constexpr uint32_t kNib = 0x000F000Fu;
-constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
-
-// workgroup barrier after this wavefront's LDS operations have completed
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// kMagic in a VGPR the compiler cannot constant-fold, so that (v & mask) | magic is
-// one v_and_or_b32
-__device__ __forceinline__ uint32_t opaque_magic() {
-  uint32_t v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "n"(kMagic));
-  return v;
-}
-
-// one packed word (codes of k = 0..7) -> bf16 128 + q in the k order 0,4,1,5,2,6,3,7
-__device__ __forceinline__ u32x4_t unpack_word(uint32_t w, uint32_t magic) {
-  u32x4_t b;
-  b[0] = (w & kNib) | magic;
-  b[1] = ((w >> 4) & kNib) | magic;
-  b[2] = ((w >> 8) & kNib) | magic;
-  b[3] = ((w >> 12) & kNib) | magic;
-  return b;
-}
 
 // What one lane loads for one stage.
 struct StageData {

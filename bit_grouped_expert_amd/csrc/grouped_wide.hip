@@ -1,0 +1,344 @@
+// Wide-tile grouped GEMM over groupwise-affine 4-bit weights for gfx950 (MI355X): the
+// engine for large groups (hundreds of rows per expert), where the layer is bound by
+// the matrix cores and the vector work around them rather than by weight bytes.
+//
+// Pages: MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference
+// engine for Qwen3.6-35B-A3B on Apple Silicon", body paragraph 5 (4-bit weights
+// with one bf16 scale and bias per 64, reconstructed tile by tile inside the
+// grouped GEMM, with fp32 accumulation).
+//
+// Arithmetic: as in the resident-tile engine (exact up to fp32 rounding): per 64-wide
+// group, P' = sum x (128 + q) on the matrix cores from zero, acc += s P', and the bias
+// term (b - 128 s) X as an fp32 matrix-core product with the stage's four groups as k.
+//
+// Work decomposition.  One workgroup per tile of up to 128 rows of one group (eight
+// 16-row fragments); it walks every block of 256 weight rows (with SwiGLU: 128 gate
+// rows and the matching 128 up rows) as one sequence of 256-K stages.  Each of the
+// eight wavefronts owns two 16-row weight fragments of the block (SwiGLU: a gate
+// fragment and its up fragment) for all eight row fragments, so that a packed word,
+// unpacked once, feeds eight MFMAs, and the per-group fold costs two FMAs per MFMA.
+// Weights stream from HBM into VGPRs as in the resident engine (16-byte loads of whole
+// 128-byte row lines, two stages in flight, two permlane32 swaps per word quad).  The
+// tile's activation rows go through two LDS buffers of one stage each, by direct
+// global->LDS loads issued one stage ahead.  The two buffers are distinct LDS arrays
+// addressed statically (the stage loop is unrolled by two), so the compiler can tell
+// that a direct load into one does not feed the reads of the other and does not wait
+// for it before them; each wavefront drains its loads before the stage's barrier,
+// which costs little since they were issued a whole stage earlier.  The row sums X
+// come from the first block's stages (activation fragments times ones) and stay in
+// LDS for the later blocks.  Tiles of one group are adjacent and XCD b % 8 takes a
+// contiguous run of tiles, so a group's weights are read from HBM about once per XCD.
+//
+// Measured at 8192 tokens it is no faster than the resident engine (gate_up 682 us):
+// timing variants put a full tile near 4 us per stage against 1.7 us of bf16 matrix
+// work; without any global load in the loop it still takes 514 us, and dropping the
+// fold, the unpacking or the LDS activation reads each changes little.  The fp32 bias
+// product (a quarter of the bf16 matrix time), the dependent chain of each fragment's
+// two MFMAs and its fold, and four rounds of tiles for 3.05 rounds of work account for
+// most of it.
+#include "common.h"
+#include "internal.h"
+#include "q4_stream.h"
+
+namespace moeq4 {
+
+namespace {
+
+constexpr int WBM = kWideBM;                 // rows per tile
+constexpr int WKS = 256;                     // K per stage (four groups)
+constexpr int A_BUF = (WBM / 16) * 32 * 256; // [fragment 8][16-byte chunk 32][row 16]: 64 KB
+constexpr int XS_FLOATS = (kWideMaxK / 64) * WBM;  // X, fp32 [K / 64][128 rows]
+constexpr int STG_BYTES = 8 * 1024;          // epilogue staging, 1 KB per wavefront
+static_assert(2 * A_BUF + 4 * XS_FLOATS + STG_BYTES <= 160 * 1024, "LDS budget");
+
+struct WideLds {
+  unsigned char* a[2];
+  float* xs;
+  unsigned char* stg;
+};
+
+template <bool SWIGLU, int GS>
+__device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& lds) {
+  constexpr int D = 2;  // weight register sets: the next stage's in flight
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = l & 15, q = l >> 4;
+  const int N = p.N, K = p.K, KW = K >> 3, KG = K >> 6, NK = K / WKS;
+  const int NB = SWIGLU ? (N >> 1) / 128 : N / 256;
+  const int UT = NB * NK;  // stages of the whole tile: block blk, stage st at blk * NK + st
+
+  // ---- this workgroup's tile: XCD b % 8 takes a contiguous run of tiles
+  const int cnt = *p.tile_count;
+  const int per = (cnt + 7) >> 3;
+  const int jx = blockIdx.x >> 3;
+  if (jx >= per) return;  // uniform, before any barrier
+  const int tile = (blockIdx.x & 7) * per + jx;
+  if (tile >= cnt) return;
+  const int4 tt = p.tiles[tile];
+  const int grp = __builtin_amdgcn_readfirstlane(tt.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(tt.y);
+  const int nrows = __builtin_amdgcn_readfirstlane(tt.z);
+  const int nfv = (nrows + 15) >> 4;  // row fragments with rows (1..8)
+  const bool in_main = grp < p.n_main;
+  const int gi = in_main ? grp : 0;
+  const uint32_t* Wq = (in_main ? p.main.q : p.last.q) + (int64_t)gi * N * KW;
+  const uint16_t* Ws = (in_main ? p.main.s : p.last.s) + (int64_t)gi * N * KG;
+  const uint16_t* Wb = (in_main ? p.main.b : p.last.b) + (int64_t)gi * N * KG;
+
+  // ---- activation rows: wavefront w loads fragment w (rows 16 w + m); rows past the
+  // tile repeat its last row, rows outside [0, a_rows) read row a_rows (zero)
+  const uint16_t* asrc;
+  {
+    const int r = min(16 * wave + m, nrows - 1);
+    int a = p.a_row_index ? p.a_row_index[row0 + r] : row0 + r;
+    if (a < 0 || a >= p.a_rows) a = p.a_rows;
+    asrc = p.A + (int64_t)a * K + 8 * q;
+  }
+  // stage st of the activations into buffer dst: chunks 4 cb .. 4 cb + 3 of fragment
+  // `wave` per load (1 KB)
+  auto issue_a = [&](int st, unsigned char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      __builtin_amdgcn_global_load_lds(asrc + WKS * st + 32 * cb, dst + wave * 8192 + cb * 1024, 16, 0,
+                                       0);
+  };
+
+  // ---- weight stream: flat stage index, past the end the last stage again
+  int pf_v = 0;
+  auto pf_load = [&](StageW& w) __attribute__((always_inline)) {
+    const int v = min(pf_v, UT - 1);
+    const int blk = v / NK, st = v - blk * NK;
+    int n0, n1;
+    if (SWIGLU) {
+      const int u = 8 * blk + wave;
+      n0 = 16 * u + m;
+      n1 = (N >> 1) + 16 * u + m;
+    } else {
+      n0 = 256 * blk + 32 * wave + m;
+      n1 = n0 + 16;
+    }
+    const uint32_t co0 = ((uint32_t)n0 * KW + 4 * q) * 4u, co1 = ((uint32_t)n1 * KW + 4 * q) * 4u;
+    const uint32_t so0 = (uint32_t)n0 * KG * 2u, so1 = (uint32_t)n1 * KG * 2u;
+    const uint32_t* qs = Wq + 32 * st;
+    w.c[0][0] = ld<u32x4_t>(qs, co0);
+    w.c[0][1] = ld<u32x4_t>(qs + 16, co0);
+    w.s[0] = ld<u32x2_t>(Ws + 4 * st, so0);
+    w.b[0] = ld<u32x2_t>(Wb + 4 * st, so0);
+    w.c[1][0] = ld<u32x4_t>(qs, co1);
+    w.c[1][1] = ld<u32x4_t>(qs + 16, co1);
+    w.s[1] = ld<u32x2_t>(Ws + 4 * st, so1);
+    w.b[1] = ld<u32x2_t>(Wb + 4 * st, so1);
+    ++pf_v;
+  };
+
+  const uint32_t magic = opaque_magic();
+  const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  uint32_t widx[4] = {(uint32_t)(4 * q), (uint32_t)(4 * q + 1), (uint32_t)(4 * q + 2),
+                      (uint32_t)(4 * q + 3)};
+  {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(widx[0], widx[2], false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(widx[1], widx[3], false, false);
+    widx[0] = r0[0];
+    widx[2] = r0[1];
+    widx[1] = r1[0];
+    widx[3] = r1[1];
+  }
+  uint32_t a_step[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a_step[t] = widx[t] * 256u + 16u * m;
+
+  f32x4_t acc[8][2];  // [row fragment][weight fragment]
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      acc[f][0] = zero;
+      acc[f][1] = zero;
+    }
+  };
+  reset();
+
+  // One 256-K stage in two 128-K halves (MFMA steps 2 (g ^ GS), 2 (g ^ GS) + 1 of a
+  // half take its scale group g, as in the resident engine): per row fragment, P' of
+  // both weight fragments and both groups from zero, then acc += s P'.  cbq: the
+  // lane's (b - 128 s) of group q of the stage, for the bias term.
+  auto compute = [&](const StageW& w, const unsigned char* abuf, float* cbq) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t sw = (q & 2) ? w.s[j][1] : w.s[j][0];
+      const uint32_t bw = (q & 2) ? w.b[j][1] : w.b[j][0];
+      const float sq = (q & 1) ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
+      const float bq = (q & 1) ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
+      cbq[j] = fmaf(-128.f, sq, bq);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const unsigned char* ab = abuf + hh * 4096;
+      u32x4_t wsw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wsw[j] = swap_quad(w.c[j][hh]);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        u32x4_t B[2][2];  // [weight fragment][half step]
+        float sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) B[j][h] = unpack_word(wsw[j][2 * (g ^ GS) + h], magic);
+          sc[j] = g == 0 ? bf16lo_to_f32(w.s[j][hh]) : bf16hi_to_f32(w.s[j][hh]);
+        }
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          if (f < nfv) {
+            const u32x4_t a0 = *(const u32x4_t*)(ab + f * 8192 + a_step[2 * (g ^ GS)]);
+            const u32x4_t a1 = *(const u32x4_t*)(ab + f * 8192 + a_step[2 * (g ^ GS) + 1]);
+            f32x4_t P[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) P[j] = mfma16x16x32(a0, B[j][0], zero);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) P[j] = mfma16x16x32(a1, B[j][1], P[j]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(sc[j], P[j][i], acc[f][j][i]);
+          }
+        }
+      }
+    }
+  };
+  // X[group][row] of this wavefront's fragment for the stage's four groups: the product
+  // of the group's two 32-K activation fragments with a fragment of ones, written by
+  // the lanes of column 0
+  float* xs = lds.xs;
+  auto row_sums = [&](int st, const unsigned char* abuf) __attribute__((always_inline)) {
+    if (wave < nfv) {
+      const unsigned char* af = abuf + wave * 8192 + 16 * m;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x4_t a0 = *(const u32x4_t*)(af + (8 * g4 + q) * 256);
+        const u32x4_t a1 = *(const u32x4_t*)(af + (8 * g4 + 4 + q) * 256);
+        const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
+        if (m == 0) *(f32x4_t*)(xs + (4 * st + g4) * WBM + 16 * wave + 4 * q) = X;
+      }
+    }
+  };
+  // acc += (b - 128 s) X over the stage's four groups (v_mfma_f32_16x16x4_f32: lane l
+  // gives A[row l % 16][k = l / 16] and B[k = l / 16][column l % 16], k = group)
+  auto bias_term = [&](int st, const float* cbq) __attribute__((always_inline)) {
+    const float* xg = xs + (4 * st + q) * WBM + m;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f < nfv) {
+        const float xa = xg[16 * f];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, cbq[j], acc[f][j], 0, 0, 0);
+      }
+    }
+  };
+  // the finished block: bf16 rows through this wavefront's 1 KB of LDS staging
+  unsigned char* stg = lds.stg + wave * 1024;
+  auto epilogue = [&](int blk) __attribute__((always_inline)) {
+    uint16_t* cs = (uint16_t*)stg;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f < nfv) {
+        if (SWIGLU) {
+          const int col = p.c_perm ? ((m & 8) | perm8(m & 7)) : m;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gte = acc[f][0][i], up = acc[f][1][i];
+            cs[(4 * q + i) * 16 + col] = to_bf16(gte / (1.f + __expf(-gte)) * up);
+          }
+          const int r = l >> 1, half = l & 1;
+          const int u = 8 * blk + wave;
+          if (l < 32 && 16 * f + r < nrows)
+            *(u32x4_t*)(p.C + (int64_t)(row0 + 16 * f + r) * p.ldc + 16 * u + 8 * half) =
+                *(const u32x4_t*)(cs + r * 16 + 8 * half);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cs[(4 * q + i) * 32 + 16 * j + m] = to_bf16(acc[f][j][i]);
+          const int r = l >> 2, piece = l & 3;
+          if (16 * f + r < nrows)
+            *(u32x4_t*)(p.C + (int64_t)(row0 + 16 * f + r) * p.ldc + 256 * blk + 32 * wave + 8 * piece) =
+                *(const u32x4_t*)(cs + r * 32 + 8 * piece);
+        }
+      }
+    }
+  };
+
+  // ---- prologue: stage 0's activations and weights
+  StageW W[D];
+  issue_a(0, lds.a[0]);
+  pf_load(W[0]);
+  wait_vmcnt0();
+  lds_barrier();
+
+  // ---- stage loop: stage v in buffer v & 1 and register set v & 1.  The next stage's
+  // activations and weights are issued first; after the matrix work every load has
+  // landed and a barrier publishes the next buffer.  The bias term of stage v follows
+  // the barrier (X of a first block's stage is formed during it); after a block's last
+  // stage its outputs, then the accumulators start over.
+  auto step = [&](int v, const unsigned char* cur_a, unsigned char* next_a, StageW& cur,
+                  StageW& fresh) __attribute__((always_inline)) {
+    const int blk = v / NK, st = v - blk * NK;
+    const int vn = v + 1 < UT ? v + 1 : v;  // the last stage loads itself again
+    issue_a(vn - (vn / NK) * NK, next_a);
+    pf_load(fresh);
+    float cbq[2];
+    compute(cur, cur_a, cbq);
+    if (blk == 0) row_sums(st, cur_a);
+    wait_vmcnt0();
+    lds_barrier();
+    bias_term(st, cbq);
+    if (st == NK - 1) {
+      epilogue(blk);
+      reset();
+    }
+  };
+  int v = 0;
+  for (; v + 2 <= UT; v += 2) {
+    step(v, lds.a[0], lds.a[1], W[0], W[1]);
+    step(v + 1, lds.a[1], lds.a[0], W[1], W[0]);
+  }
+  if (v < UT) step(v, lds.a[0], lds.a[1], W[0], W[1]);
+}
+
+// GS: scale group of MFMA steps 0 and 1 after the word swaps, read off the swapped
+// word numbers on entry (both orders compiled).
+template <bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char a0[A_BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char a1[A_BUF];
+  __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
+  __shared__ __attribute__((aligned(16))) unsigned char stg[STG_BYTES];
+  const WideLds lds{{a0, a1}, xs, stg};
+  const int l = threadIdx.x & 63;
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
+                                                  false, false);
+  const int gs = __builtin_amdgcn_readfirstlane((int)(r[0] >> 3));
+  if (gs) wide_body<SWIGLU, 1>(p, lds);
+  else wide_body<SWIGLU, 0>(p, lds);
+}
+
+template <bool SWIGLU>
+void launch_w(const TiledParams& p, int64_t n_tiles_bound, hipStream_t s) {
+  const int64_t grid = ((n_tiles_bound > 0 ? n_tiles_bound : 1) + 7) / 8 * 8;
+  hipLaunchKernelGGL((q4_wide_kernel<SWIGLU>), dim3((unsigned)grid), dim3(512), 0, s, p);
+}
+
+}  // namespace
+
+bool wide_supported(int N, int K, bool swiglu, int a_rows) {
+  (void)swiglu;  // SwiGLU: 128 gate rows and 128 up rows per block, so N % 256 as well
+  return a_rows >= 1 && K > 0 && K % WKS == 0 && K <= kWideMaxK && N > 0 && N % 256 == 0;
+}
+
+void launch_wide(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s) {
+  if (swiglu) launch_w<true>(p, n_tiles_bound, s);
+  else launch_w<false>(p, n_tiles_bound, s);
+}
+
+}  // namespace moeq4

@@ -168,6 +168,16 @@ struct TiledParams {
 bool tiled_supported(int N, int K, bool swiglu, int a_rows);
 void launch_tiled(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
 
+// Wide-tile engine (grouped_wide.hip), for large groups: one workgroup per tile of up
+// to 128 rows (tile map built with bm = kWideBM), weights streamed into VGPRs, the
+// tile's activations through two LDS stage buffers.  Same A, C and c_perm conventions
+// as the resident engine; needs K % 256 == 0, K <= kWideMaxK, N % 256 == 0 (SwiGLU:
+// N = 2F with F % 128 == 0) and a_rows >= 1; C rows are written with 16-byte stores.
+constexpr int kWideBM = 128;
+constexpr int kWideMaxK = 2048;
+bool wide_supported(int N, int K, bool swiglu, int a_rows);
+void launch_wide(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
                     const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);

@@ -35,7 +35,7 @@ def torch_cuda():
     return torch
 
 
-ENGINES = ["rows", "grouped", "stream", "resident", "tiled"]
+ENGINES = ["rows", "grouped", "stream", "resident", "tiled", "wide"]
 
 
 @pytest.fixture
@@ -365,7 +365,7 @@ def test_layer_forward_parity_full(torch_cuda, name):
     _layer_full_check(torch_cuda, cfg)
 
 
-@pytest.mark.parametrize("engine", ["rows", "grouped", "stream", "tiled"], indirect=True)
+@pytest.mark.parametrize("engine", ["rows", "grouped", "stream", "tiled", "wide"], indirect=True)
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_layer_forward_parity_full_rows(torch_cuda, name, engine):
     """The same layers through the engines the default does not pick for them."""
