@@ -13,6 +13,10 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr float kRefineGap = 1e-4f;
+// average rows per group from which the wide-tile engine is the default (measured: at
+// 8192 tokens, about 290 rows per group, 955 against 964 us for both GEMMs; at 32768,
+// 3.06 against 3.29 ms)
+constexpr int64_t kWideMinAvgRows = 192;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -43,9 +47,10 @@ moe_status check_shape(const moe_shape* s) {
 //            weight rows, both operands staged through LDS per 64-K stage, the
 //            weights unpacked once per workgroup (measured no faster than resident
 //            at 8192 tokens: bound by LDS traffic; not a default).
-//   wide     (K % 256 == 0, K <= 2048, N % 256 == 0): tiles of 128 rows, weights
-//            streamed into VGPRs, each packed word feeding eight row fragments, the
-//            activations through two LDS stage buffers.
+//   wide     (default when groups average at least 192 rows; K % 256 == 0,
+//            K <= 2048, N % 256 == 0): tiles of 128 rows, weights streamed into VGPRs,
+//            each packed word feeding eight row fragments, the activations through two
+//            LDS stage buffers.
 // The environment variable MOEQ4_GEMM=resident|stream|grouped|rows|tiled|wide forces one
 // (for measurement and tests; an engine that cannot take the shapes falls back to
 // grouped).
@@ -65,6 +70,7 @@ GemmPlan plan_gemm(int64_t rows, int n_groups, bool stream_ok, bool resident_ok,
   if (env && strcmp(env, "stream") == 0 && stream_ok)
     return GemmPlan{ENG_STREAM, rows >= 48 * g ? 64 : 32};
   if (env && strcmp(env, "resident") == 0 && resident_ok) return GemmPlan{ENG_RESIDENT, kResidentBM};
+  if (!env && wide_ok && rows >= kWideMinAvgRows * g) return GemmPlan{ENG_WIDE, kWideBM};
   if (!env && resident_ok) return GemmPlan{ENG_RESIDENT, kResidentBM};
   return GemmPlan{ENG_GROUPED, kGroupedBM};
 }

@@ -187,20 +187,38 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
           for (int h = 0; h < 2; ++h) B[j][h] = unpack_word(wsw[j][2 * (g ^ GS) + h], magic);
           sc[j] = g == 0 ? bf16lo_to_f32(w.s[j][hh]) : bf16hi_to_f32(w.s[j][hh]);
         }
+        // two row fragments at a time in three phases kept apart by scheduling barriers
+        // (operands; the four MFMA chains; the folds), so that four independent chains
+        // are in flight and no result is consumed before the chains are issued.  A pair
+        // past the tile's last fragment computes rows it then drops.
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          if (f < nfv) {
-            const u32x4_t a0 = *(const u32x4_t*)(ab + f * 8192 + a_step[2 * (g ^ GS)]);
-            const u32x4_t a1 = *(const u32x4_t*)(ab + f * 8192 + a_step[2 * (g ^ GS) + 1]);
-            f32x4_t P[2];
+        for (int fp = 0; fp < 4; ++fp) {
+          if (2 * fp < nfv) {
+            u32x4_t a[2][2];  // [fragment of the pair][half step]
 #pragma unroll
-            for (int j = 0; j < 2; ++j) P[j] = mfma16x16x32(a0, B[j][0], zero);
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) P[j] = mfma16x16x32(a1, B[j][1], P[j]);
+              for (int h = 0; h < 2; ++h)
+                a[e][h] = *(const u32x4_t*)(ab + (2 * fp + e) * 8192 + a_step[2 * (g ^ GS) + h]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t P[2][2];  // [fragment of the pair][weight fragment]
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(sc[j], P[j][i], acc[f][j][i]);
+              for (int j = 0; j < 2; ++j) P[e][j] = mfma16x16x32(a[e][0], B[j][0], zero);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) P[e][j] = mfma16x16x32(a[e][1], B[j][1], P[e][j]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[2 * fp + e][j][i] = fmaf(sc[j], P[e][j][i], acc[2 * fp + e][j][i]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
