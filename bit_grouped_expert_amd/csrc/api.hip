@@ -231,8 +231,7 @@ static moe_status route_impl(const moe_shape* shape, const uint16_t* x, const fl
   const int T = shape->T, D = shape->d_model, E = shape->n_experts, k = shape->top_k;
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
-  launch_router_split(router_w, Rs, E, D, stream);
-  launch_router_logits(x, Rs, logits, T, D, E, nullptr, stream);
+  launch_router(x, router_w, Rs, logits, T, D, E, nullptr, stream);
   launch_topk(logits, x, router_w, T, D, E, k, gap, topk_idx, topk_w, stream);
   return launch_status();
 }
@@ -474,8 +473,7 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   mark(0);
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
-  launch_router_split(router_w, Rs, E, D, stream);
-  launch_router_logits(x, Rs, logits, T, D, E,
+  launch_router(x, router_w, Rs, logits, T, D, E,
                        plan.eng == ENG_RESIDENT || plan.eng == ENG_TILED || plan.eng == ENG_WIDE
                            ? at<uint16_t>(ws, L.xprep)
                            : nullptr,

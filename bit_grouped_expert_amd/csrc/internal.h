@@ -13,6 +13,11 @@ void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t
 // the resident-tile GEMM
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s);
+// Router logits L = x R^T (fp32): with T < 2048 and D % 256 == 0 on the fp32 matrix cores
+// from R directly, otherwise R split into three bf16 planes (Rs, 3 * ceil(E/16) * 16 * D)
+// and bf16 matrix cores.  xprep as above.
+void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
+                   uint16_t* xprep, hipStream_t s);
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
                  float tau, int32_t* idx, float* w, hipStream_t s);
 

@@ -324,6 +324,132 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
   }
 }
 
+// Fewer tokens (D % 256 == 0): the fp32 matrix cores on R itself (v_mfma_f32_16x16x4_f32,
+// bf16 x widened exactly), so no split of R is needed.  Workgroup tile: 16 tokens x 32
+// experts; its eight wavefronts are two 16-expert tiles times four quarters of each
+// 256-K chunk, with two accumulators each, added through LDS at the end.  The chunk's R
+// rows (1 KB each) and x rows go through padded LDS rows with line-whole loads, one
+// chunk ahead in VGPRs.  In MFMA step s of a 16-K group, lane (m, q) supplies
+// k = 16 g + 4 q + s of token row m and of expert column m, so its operands of four
+// steps are one 16-byte read of R and one 8-byte read of x.  The workgroups of the
+// first expert column also write the prepared copy of x from the x pieces they load.
+constexpr int kF32KC = 256;
+constexpr int kF32RRow = kF32KC * 4 + 16;  // padded LDS row of R, bytes
+constexpr int kF32XRow = kF32KC * 2 + 16;  // padded LDS row of x, bytes
+__global__ __launch_bounds__(512) void router_logits_f32_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ R, float* __restrict__ L, int T, int D,
+    int E, uint16_t* __restrict__ xprep) {
+  __shared__ __attribute__((aligned(16))) unsigned char rs[2][32 * kF32RRow];
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[2][16 * kF32XRow];
+  __shared__ f32x4_t red[3][2][64];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int m = l & 15, q = l >> 4;
+  const int tile = wave & 1, kq = wave >> 1;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 32;
+  const int nch = D / kF32KC;
+  // this thread's pieces: R rows (tid / 64) + 8 i, 16-byte piece tid % 64; x row tid / 32,
+  // 16-byte piece tid % 32
+  const float* rsrc[4];
+  uint32_t rdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 6) + 8 * i;
+    rsrc[i] = R + (int64_t)min(e0 + row, E - 1) * D + 4 * (tid & 63);
+    rdst[i] = (uint32_t)(row * kF32RRow + 16 * (tid & 63));
+  }
+  const int xr = tid >> 5, xc = tid & 31;
+  const bool xv = t0 + xr < T;
+  const uint16_t* xsrc = x + (int64_t)min(t0 + xr, T - 1) * D + 8 * xc;
+  const uint32_t xdst = (uint32_t)(xr * kF32XRow + 16 * xc);
+  const bool prep = xprep != nullptr && blockIdx.y == 0;
+  // two register sets: chunk ch + 2 is loaded while ch is computed and ch + 1 is stored
+  struct Piece {
+    u32x4_t r[4], x;
+  };
+  auto load = [&](Piece& pc, int ch) __attribute__((always_inline)) {
+    ch = min(ch, nch - 1);  // past the end: the last chunk again (never stored)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pc.r[i] = *(const u32x4_t*)(rsrc[i] + ch * kF32KC);
+    pc.x = *(const u32x4_t*)(xsrc + ch * kF32KC);
+  };
+  auto store = [&](const Piece& pc, int ch, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)(&rs[buf][rdst[i]]) = pc.r[i];
+    *(u32x4_t*)(&xsh[buf][xdst]) = pc.x;
+    if (prep && xv) *(u32x4_t*)(xprep + (int64_t)(t0 + xr) * D + ch * kF32KC + 8 * xc) = interleave8(pc.x);
+  };
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const unsigned char* rb = &rs[buf][(16 * tile + m) * kF32RRow + kq * 256];
+    const unsigned char* xb = &xsh[buf][m * kF32XRow + kq * 128];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t rv = *(const f32x4_t*)(rb + (16 * g + 4 * q) * 4);
+      const u32x2_t xw = *(const u32x2_t*)(xb + (16 * g + 4 * q) * 2);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo_to_f32(xw[0]), rv[0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi_to_f32(xw[0]), rv[1], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo_to_f32(xw[1]), rv[2], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi_to_f32(xw[1]), rv[3], acc1, 0, 0, 0);
+    }
+  };
+  // chunk ch in buffer ch & 1; the other buffer was last read in the previous chunk,
+  // before the last barrier
+  auto step = [&](int ch, Piece& next, Piece& fresh) __attribute__((always_inline)) {
+    load(fresh, ch + 2);
+    compute(ch & 1);
+    if (ch + 1 < nch) {
+      store(next, ch + 1, (ch & 1) ^ 1);
+      __syncthreads();
+    }
+  };
+  Piece p0, p1;
+  load(p0, 0);
+  load(p1, 1);
+  store(p0, 0, 0);
+  __syncthreads();
+  int ch = 0;
+  for (; ch + 2 <= nch; ch += 2) {
+    step(ch, p1, p0);
+    step(ch + 1, p0, p1);
+  }
+  if (ch < nch) step(ch, p1, p0);
+  if (xprep && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) {
+    // the zero row after the last token
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int c = l; c < (D >> 3); c += 64) *(u32x4_t*)(xprep + (int64_t)T * D + 8 * c) = zero;
+  }
+  f32x4_t acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = acc0[i] + acc1[i];
+  if (kq > 0) red[kq - 1][tile][l] = acc;
+  __syncthreads();
+  const int e = e0 + 16 * tile + m;
+  if (kq == 0 && e < E) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const f32x4_t o = red[j][tile][l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += o[i];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = t0 + 4 * q + r;
+      if (tt < T) L[(int64_t)tt * E + e] = acc[r];
+    }
+  }
+}
+
+void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
+                   uint16_t* xprep, hipStream_t s) {
+  if (T < 2048 && D % kF32KC == 0) {
+    dim3 grid((T + 15) / 16, (E + 31) / 32);
+    hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(512), 0, s, x, R, L, T, D, E, xprep);
+    return;
+  }
+  launch_router_split(R, Rs, E, D, s);
+  launch_router_logits(x, Rs, L, T, D, E, xprep, s);
+}
+
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s) {
   dim3 block(512);
