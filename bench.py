@@ -37,6 +37,9 @@ KERNEL_LABEL = {
     "prefill512": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
     "decode1": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
     "decode4": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
+    "uniform8192": "grouped gate_up + SwiGLU (q4_wide_kernel<true>)",
+    "zipf8192": "grouped gate_up + SwiGLU (q4_wide_kernel<true>)",
+    "long32768": "grouped gate_up + SwiGLU (q4_wide_kernel<true>)",
 }
 
 # counters of a plain copy kernel of known size, read in the same rocprofv3 --pmc runs
@@ -44,8 +47,8 @@ KERNEL_LABEL = {
 TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over `bench.py --config prefill512 --steps 2
     # --warmup 1 --no-cpu-baseline --copy-probe` (summary in profiles/)
-    "prefill512": {"fetch_kib": 171895.7, "write_kib": 4608.4,
-                   "copy_fetch_kib": 524325.5, "copy_write_kib": 1048576.0, "copy_bytes": 2 ** 30},
+    "prefill512": {"fetch_kib": 172462.8, "write_kib": 4608.5,
+                   "copy_fetch_kib": 524323.4, "copy_write_kib": 1048576.0, "copy_bytes": 2 ** 30},
 }
 
 
