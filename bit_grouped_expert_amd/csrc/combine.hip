@@ -6,7 +6,8 @@
 // 4) name the shared expert that sees every token; applying the routing weight
 // after the down projection and giving the shared expert unit weight are
 // readings.  The kernel streams Y once with 128-bit loads: one workgroup per
-// (token, 2048-column slice), eight columns per thread.
+// (token, 2048-column slice), eight columns per thread, up to eight slots' rows in
+// flight.
 #include "common.h"
 #include "internal.h"
 
@@ -33,15 +34,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = slot_row[(int64_t)t * k + j];
-    const float wj = w[(int64_t)t * k + j];
-    if (r < 0 || r >= y_rows) continue;
-    const u32x4_t v = *(const u32x4_t*)(Y + (int64_t)r * D + d0);
+  // slots in batches of eight: every row of a batch is loaded before any is added (in
+  // slot order), so that eight loads are in flight
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    u32x4_t v[8];
+    float wj[8];
+    bool okj[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      acc[2 * h] = fmaf(wj, bf16lo_to_f32(v[h]), acc[2 * h]);
-      acc[2 * h + 1] = fmaf(wj, bf16hi_to_f32(v[h]), acc[2 * h + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int32_t r = j < k ? slot_row[(int64_t)t * k + j] : -1;
+      const bool ok = r >= 0 && r < y_rows;
+      okj[u] = ok;
+      wj[u] = ok ? w[(int64_t)t * k + j] : 0.f;
+      v[u] = ok ? *(const u32x4_t*)(Y + (int64_t)r * D + d0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (okj[u]) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] = fmaf(wj[u], bf16lo_to_f32(v[u][h]), acc[2 * h]);
+          acc[2 * h + 1] = fmaf(wj[u], bf16hi_to_f32(v[u][h]), acc[2 * h + 1]);
+        }
+      }
     }
   }
   u32x4_t o;
