@@ -473,9 +473,6 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
 __device__ __forceinline__ float unordered_bits(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
-__device__ __forceinline__ uint64_t rank_key(float v, int e) {
-  return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
 __device__ __forceinline__ uint64_t ordered_bits64(double v) {
   uint64_t u = (uint64_t)__double_as_longlong(v);
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
@@ -509,13 +506,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
   }));
 }
-// the largest 64-bit key of the wavefront: the largest high word, then the largest
-// low word among the lanes that hold it
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
-  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // (value, expert) pair order: larger value first, then lower expert id.
 struct Cand {
@@ -540,25 +530,40 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
   const float* Lt = L + (int64_t)t * E;
 
   float val[MAXC];
-  uint64_t key[MAXC];
+  uint32_t key[MAXC];  // order-preserving bits of the logit (at least 1); 0 once selected
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     int e = c * 64 + lane;
     val[c] = e < E ? Lt[e] : 0.f;
-    key[c] = e < E ? rank_key(val[c], e) : 0ull;
+    key[c] = e < E ? max(ordered_bits(val[c]), 1u) : 0u;
   }
 
-  // lane j keeps the j-th selection
+  // lane j keeps the j-th selection.  A round takes the largest logit of the wavefront
+  // (one 32-bit reduction); only when several lanes hold it does a second reduction pick
+  // the lowest expert id among them.  Within a lane the lower slot (lower id) wins ties.
   int my_e = -1;
   float my_v = 0.f;
   const int nsel = (k + 1 < E) ? k + 1 : E;
   for (int j = 0; j < nsel; ++j) {
-    uint64_t best = 0;
+    uint32_t lb = key[0];
+    int lc = 0;
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_key(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const float v = unordered_bits((uint32_t)(best >> 32));
+    for (int c = 1; c < MAXC; ++c)
+      if (key[c] > lb) {
+        lb = key[c];
+        lc = c;
+      }
+    const uint32_t hi = wave_max_u32(lb);
+    const uint64_t holders = __ballot(lb == hi);
+    int e;
+    if (__popcll(holders) == 1) {
+      const int wl = __builtin_ctzll(holders);
+      e = 64 * __builtin_amdgcn_readlane(lc, wl) + wl;
+    } else {
+      const uint32_t r = wave_max_u32(lb == hi ? 0xFFFFFFFFu - (uint32_t)(64 * lc + lane) : 0u);
+      e = (int)(0xFFFFFFFFu - r);
+    }
+    const float v = unordered_bits(hi);
     if (lane == j) {
       my_e = e;
       my_v = v;
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
     if ((e & 63) == lane) {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c)
-        if (c == (e >> 6)) key[c] = 0ull;
+        if (c == (e >> 6)) key[c] = 0u;
     }
   }
 
