@@ -269,13 +269,11 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     }
   };
 
-  // ---- prologue: D - 1 stages in flight.  Every wavefront issues the same loads for
-  // every stage, also past the end of its stream (those reload a valid stage and are
-  // never used), so that the compiler's wait counts stay exact across the loop.
+  // ---- weight register sets, D - 1 stages in flight from the prologue (issued with the
+  // first tile below).  Every wavefront issues the same loads for every stage, also past
+  // the end of its stream (those reload a valid stage and are never used), so that the
+  // compiler's wait counts stay exact across the loop.
   StageW W[D];
-  pf_chunk();
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d) pf_load(W[d]);
 
   // One chunk: NST stages, stage s on register set s (D == NST, so the rotation starts
   // over with every chunk).  The loads stay outside the branch on the fragment count:
@@ -310,7 +308,55 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     }
   };
 
-  int cur_seg = -1;
+  // X[group][row] of the tile: the product of each group's two 32-K activation fragments
+  // with a fragment of ones, written by the lanes of column 0; then a barrier
+  auto tile_row_sums = [&](int nfv) __attribute__((always_inline)) {
+    float* xw = (float*)(smem + xs_off(K));
+    const int KG4 = K >> 6;
+    for (int pi = wave; pi < nfv * KG4; pi += 8) {
+      const int f = pi / KG4, g = pi - f * KG4;
+      const unsigned char* ab = smem + f * A_FRAG + (8 * g + 2 * q) * 256 + 16 * m;
+      const u32x4_t a0 = *(const u32x4_t*)ab;
+      const u32x4_t a1 = *(const u32x4_t*)(ab + 256);
+      const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
+      if (m == 0) *(f32x4_t*)(xw + g * 32 + 16 * f + 4 * q) = X;
+    }
+    lds_barrier();
+  };
+
+  // ---- the first tile's activation rows go through VGPRs, loaded before the weight
+  // prologue: waiting for them then leaves the weight loads in flight (after direct
+  // loads into LDS, the first LDS read would wait for every load issued before it)
+  const int per_f = K >> 5;  // 1 KB pieces (32 K of 16 rows) per activation fragment
+  int cur_seg;
+  {
+    const int4 t = seg_of(c_begin);
+    const int nf0 = t.z > 16 ? 2 : 1;
+    u32x4_t a_first[2][8];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int arow = idxt[t.w * 32 + 16 * f + m];
+      const uint16_t* src = p.A + (int64_t)arow * K + 8 * q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cb = wave + 8 * i;
+        if (f < nf0 && cb < per_f) a_first[f][i] = *(const u32x4_t*)(src + 32 * cb);
+      }
+    }
+    pf_chunk();
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) pf_load(W[d]);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cb = wave + 8 * i;
+        if (f < nf0 && cb < per_f) *(u32x4_t*)(smem + f * A_FRAG + cb * 1024 + 16 * l) = a_first[f][i];
+      }
+    lds_barrier();
+    tile_row_sums(nf0);
+    cur_seg = t.w;
+  }
   for (int ch = c_begin; ch < c_end; ++ch) {
     const int4 t = seg_of(ch);
     const int k = t.w, row0 = t.y, nrows = t.z;
@@ -319,8 +365,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     if (k != cur_seg) {
       // the tile's activation rows for the whole K: fragment f, 16-byte chunks
       // 4 cb .. 4 cb + 3 of its 16 rows per direct load (1 KB of LDS)
-      if (cur_seg >= 0) lds_barrier();  // every wavefront is done with the previous tile
-      const int per_f = K >> 5;
+      lds_barrier();  // every wavefront is done with the previous tile
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         if (f < nfv) {
@@ -333,21 +378,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       }
       wait_vmcnt0();
       lds_barrier();
-      // X[group][row] of the tile: the product of each group's two 32-K activation
-      // fragments with a fragment of ones, written by the lanes of column 0
-      {
-        float* xw = (float*)(smem + xs_off(K));
-        const int KG4 = K >> 6;
-        for (int pi = wave; pi < nfv * KG4; pi += 8) {
-          const int f = pi / KG4, g = pi - f * KG4;
-          const unsigned char* ab = smem + f * A_FRAG + (8 * g + 2 * q) * 256 + 16 * m;
-          const u32x4_t a0 = *(const u32x4_t*)ab;
-          const u32x4_t a1 = *(const u32x4_t*)(ab + 256);
-          const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
-          if (m == 0) *(f32x4_t*)(xw + g * 32 + 16 * f + 4 * q) = X;
-        }
-      }
-      lds_barrier();
+      tile_row_sums(nfv);
       cur_seg = k;
     }
 #pragma unroll
