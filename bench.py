@@ -51,8 +51,8 @@ KERNEL_LABEL = {
 TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over `bench.py --config prefill512 --steps 2
     # --warmup 1 --no-cpu-baseline --copy-probe` (summary in profiles/)
-    "prefill512": {"fetch_kib": 172462.8, "write_kib": 4608.5,
-                   "copy_fetch_kib": 524323.4, "copy_write_kib": 1048576.0, "copy_bytes": 2 ** 30},
+    "prefill512": {"fetch_kib": 172137.6, "write_kib": 4609.0,
+                   "copy_fetch_kib": 524325.2, "copy_write_kib": 1048576.0, "copy_bytes": 2 ** 30},
 }
 
 
