@@ -280,8 +280,12 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
     launch_scan(at<int32_t>(ws, L.chunk_cnt), 0, shape->n_experts, offsets, -1, stream);
     return launch_status();
   }
-  permute_impl(shape, topk_idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt), -1,
-               stream);
+  if (permute_experts_ok(shape->T, shape->top_k, shape->n_experts))
+    launch_permute_experts(topk_idx, shape->T, shape->top_k, shape->n_experts, offsets, sorted_tok,
+                           slot_row, -1, 1, nullptr, nullptr, stream);
+  else
+    permute_impl(shape, topk_idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt), -1,
+                 stream);
   return launch_status();
 }
 
@@ -481,7 +485,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   launch_topk(logits, x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
   mark(1);
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
-  if (permute_small_ok(T, E)) {
+  if (permute_experts_ok(T, k, E)) {
+    launch_permute_experts(idx, T, k, E, offsets, sorted_tok, slot_row, has_shared ? T : -1,
+                           plan.bm, tiles, tile_count, stream);
+  } else if (permute_small_ok(T, E)) {
     launch_permute_small(idx, T, k, E, offsets, sorted_tok, slot_row, has_shared ? T : -1,
                          plan.bm, tiles, tile_count, stream);
   } else {

@@ -23,6 +23,7 @@ void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D
 
 // ---------------------------------------------------------------- permutation
 constexpr int kChunkTokens = 256;  // tokens per histogram / scatter chunk
+constexpr int kMaxTopK = 32;       // largest top_k the shape check accepts
 inline int n_chunks(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
 void launch_count(const int32_t* idx, int T, int k, int E, int32_t* chunk_cnt, hipStream_t s);
 void launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
@@ -63,8 +64,14 @@ inline int64_t max_tiles(int64_t rows_total, int n_groups, int bm) {
 }
 void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, int bm, int4* tiles,
                         int32_t* tile_count, hipStream_t s);
-// Histogram, scan, stable scatter and tile map in one single-workgroup launch (T <= 1024).
-// Same results as launch_count + launch_scan + launch_scatter + launch_build_tiles.
+// Histogram, scan, stable scatter and tile map with one workgroup per four experts
+// (T * k <= 8192, E <= 1024); with tiles == NULL no tile map is written.  Same results
+// as launch_count + launch_scan + launch_scatter + launch_build_tiles.
+bool permute_experts_ok(int T, int k, int E);
+void launch_permute_experts(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                            int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,
+                            int4* tiles, int32_t* tile_count, hipStream_t s);
+// The same in one single-workgroup launch (T <= 1024).
 bool permute_small_ok(int T, int E);
 void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,

@@ -19,6 +19,15 @@
 
 namespace moeq4 {
 
+// The k (<= 16) expert ids of token t, all loaded before any is used: one independent
+// load per slot, so that they are in flight together (a load followed by its use in a
+// loop is otherwise waited for one slot at a time).
+__device__ __forceinline__ void load_slots(const int32_t* __restrict__ idx, int t, int k,
+                                           int32_t (&e)[kMaxTopK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) e[j] = j < k ? idx[(int64_t)t * k + j] : -1;
+}
+
 // ---------------------------------------------------------------------------- count
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                     int E, int32_t* __restrict__ chunk_cnt) {
@@ -27,9 +36,12 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   __syncthreads();
   const int t = blockIdx.x * kChunkTokens + threadIdx.x;
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)t * k + j];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    int32_t ev[kMaxTopK];
+    load_slots(idx, t, k, ev);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int e = ev[j];
+      if (j < k && e >= 0 && e < E) atomicAdd(&hist[e], 1);
     }
   }
   __syncthreads();
@@ -119,17 +131,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * kChunkTokens + threadIdx.x;
   const unsigned long long bit = 1ull << lane;
+  int32_t ev[kMaxTopK];
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)t * k + j];
-      if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
+    load_slots(idx, t, k, ev);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int e = ev[j];
+      if (j < k && e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
     }
   }
   __syncthreads();
   if (t < T) {
     const int32_t* base = chunk_base + (int64_t)blockIdx.x * E;
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)t * k + j];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
+      const int e = ev[j];
       int32_t row = -1;
       if (e >= 0 && e < E) {
         int rank = __popcll(masks[wave * E + e] & (bit - 1ull));
@@ -237,10 +254,13 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
   __syncthreads();
   const unsigned long long bit = 1ull << lane;
+  int32_t ev[kMaxTopK];
   if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)tid * k + j];
-      if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
+    load_slots(idx, tid, k, ev);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int e = ev[j];
+      if (j < k && e >= 0 && e < E) atomicOr(&masks[wave * E + e], bit);
     }
   }
   __syncthreads();
@@ -269,8 +289,10 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   }
   __syncthreads();
   if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)tid * k + j];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
+      const int e = ev[j];
       int32_t row = -1;
       if (e >= 0 && e < E) {
         row = base[wave * E + e] + __popcll(masks[wave * E + e] & (bit - 1ull));
@@ -310,6 +332,212 @@ void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offs
   }
   hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, idx, T, k, E, offsets,
                      sorted_tok, slot_row, shared_rows, bm, tiles, cap, tile_count);
+}
+
+// ---------------------------------------------------------------------------- expert-parallel
+// Few routed pairs (T * k <= 8192): one workgroup of 256 threads per four experts, all
+// independent.  Every workgroup loads all T * k expert ids (thread i holds the contiguous
+// run of pairs i * per .. i * per + per - 1, so pair order is thread order) and histograms
+// them in LDS; one packed scan of (rows, tiles) per group then gives every group's offset
+// and first tile.  A workgroup places only the pairs of its own four experts: a packed
+// scan of the per-thread counts of those experts (16 bits each) gives each thread the
+// number of earlier pairs of each, so rows of an expert hold its tokens in ascending
+// token order.  It also writes its experts' tiles; workgroup 0 writes the offsets, the
+// tile count and slot_row = -1 for ids outside [0, E); the last workgroup writes the
+// shared group's identity rows and tiles.  The results equal those of the kernels above.
+constexpr int kEpThreads = 256;
+constexpr int kEpPer = 32;      // pairs per thread
+constexpr int kEpExperts = 4;   // experts per workgroup
+constexpr int kEpMaxE = 1024;
+
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
+  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
+  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Exclusive scan of one uint64 per thread over a 256-thread block (sums wrap mod 2^64;
+// callers keep every 16- or 32-bit field below its width).  *total = the block's sum.
+__device__ uint64_t block_exclusive_scan_u64_256(uint64_t v, uint64_t* total) {
+  __shared__ uint64_t wsum[kEpThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = shfl_up_u64(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint64_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kEpThreads / 64; ++w) {
+    const uint64_t sv = wsum[w];
+    if (w < wave) base += sv;
+    tot += sv;
+  }
+  __syncthreads();  // wsum may be reused by the next call
+  *total = tot;
+  return base + incl - v;
+}
+
+// PER: pairs per thread, a power of two with 256 * PER >= T * k (fixed at compile time,
+// so that the per-pair loops carry no uniform branches)
+template <int PER>
+__global__ __launch_bounds__(kEpThreads) void permute_experts_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_row, int shared_rows, int bm,
+    int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
+  __shared__ int cnt[kEpMaxE];
+  __shared__ int offl[kEpMaxE + 1];
+  __shared__ int ftl[kEpMaxE + 1];
+  const int tid = threadIdx.x;
+  const int n = T * k;
+  constexpr int per = PER;
+  const int f0 = tid * per;
+  int32_t ev[PER];
+  // 16-byte loads where four whole pairs are present (idx is 16-byte aligned, f0 % 4 == 0)
+#pragma unroll
+  for (int j = 0; j < PER; j += 4) {
+    if (PER % 4 == 0 && f0 + j + 4 <= n) {
+      const int4 v = *(const int4*)(idx + f0 + j);
+      ev[j] = v.x;
+      ev[j + 1] = v.y;
+      ev[j + 2] = v.z;
+      ev[j + 3] = v.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j + u < PER) ev[j + u] = f0 + j + u < n ? idx[f0 + j + u] : -1;
+    }
+  }
+  for (int g = tid; g < E; g += kEpThreads) cnt[g] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = ev[j];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // offsets and first tiles of the routed groups: thread i owns groups 4i .. 4i+3
+  int c4[4], rsum = 0, tsum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int g = 4 * tid + u;
+    c4[u] = g < E ? cnt[g] : 0;
+    rsum += c4[u];
+    tsum += (c4[u] + bm - 1) / bm;
+  }
+  uint64_t tot;
+  const uint64_t ex =
+      block_exclusive_scan_u64_256((uint64_t)(uint32_t)rsum | ((uint64_t)(uint32_t)tsum << 32), &tot);
+  {
+    int ro = (int)(uint32_t)ex, to = (int)(uint32_t)(ex >> 32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = 4 * tid + u;
+      if (g < E) {
+        offl[g] = ro;
+        ftl[g] = to;
+      }
+      ro += c4[u];
+      to += (c4[u] + bm - 1) / bm;
+    }
+  }
+  const int total = (int)(uint32_t)tot, ttot = (int)(uint32_t)(tot >> 32);
+  if (tid == 0) {
+    offl[E] = total;
+    ftl[E] = ttot;
+  }
+  __syncthreads();
+
+  if (blockIdx.x == 0) {
+    for (int g = tid; g <= E; g += kEpThreads) offsets[g] = offl[g];
+    if (tid == 0 && shared_rows >= 0) offsets[E + 1] = total + shared_rows;
+    if (tid == 0 && tiles) {
+      const int ns = shared_rows >= 0 ? (shared_rows + bm - 1) / bm : 0;
+      *tile_count = min(ttot + ns, cap);
+    }
+  }
+
+  // this workgroup's experts: ranks from a packed scan of the per-thread counts
+  const int e0 = blockIdx.x * kEpExperts;
+  uint64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = ev[j], d = e - e0;
+    if (d >= 0 && d < kEpExperts && e < E) mine += 1ull << (16 * d);
+  }
+  uint64_t unused;
+  uint64_t run = block_exclusive_scan_u64_256(mine, &unused);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (f0 + j < n) {
+      const int e = ev[j], d = e - e0;
+      if (d >= 0 && d < kEpExperts && e < E) {
+        int row = offl[e] + (int)((run >> (16 * d)) & 0xFFFFu);
+        run += 1ull << (16 * d);
+        if (row >= 0 && row < n) sorted_tok[row] = (f0 + j) / k;  // always, for consistent counts
+        else row = -1;
+        slot_row[f0 + j] = row;
+      } else if ((e < 0 || e >= E) && blockIdx.x == 0) {
+        slot_row[f0 + j] = -1;
+      }
+    }
+  }
+
+  if (tiles) {
+#pragma unroll
+    for (int d = 0; d < kEpExperts; ++d) {
+      const int e = e0 + d;
+      if (e < E) {
+        const int c = cnt[e], nt = (c + bm - 1) / bm, ft = ftl[e], lo = offl[e];
+        for (int u = tid; u < nt; u += kEpThreads) {
+          const int t = ft + u;
+          if (t < cap) tiles[t] = make_int4(e, lo + u * bm, min(bm, c - u * bm), 0);
+        }
+      }
+    }
+  }
+  if (shared_rows >= 0 && blockIdx.x == gridDim.x - 1) {
+    for (int t = tid; t < T; t += kEpThreads) sorted_tok[n + t] = t;
+    if (tiles) {
+      const int ns = (shared_rows + bm - 1) / bm;
+      for (int u = tid; u < ns; u += kEpThreads) {
+        const int t = ttot + u;
+        if (t < cap) tiles[t] = make_int4(E, total + u * bm, min(bm, shared_rows - u * bm), 0);
+      }
+    }
+  }
+}
+
+bool permute_experts_ok(int T, int k, int E) {
+  return T >= 1 && k >= 1 && (int64_t)T * k <= (int64_t)kEpThreads * kEpPer && E >= 1 &&
+         E <= kEpMaxE;
+}
+
+void launch_permute_experts(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                            int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,
+                            int4* tiles, int32_t* tile_count, hipStream_t s) {
+  int cap = 0;
+  if (tiles) {
+    const int n_groups = E + (shared_rows >= 0 ? 1 : 0);
+    const int rows_total = T * k + (shared_rows >= 0 ? shared_rows : 0);
+    cap = (int)max_tiles(rows_total, n_groups, bm);
+  }
+  const int grid = (E + kEpExperts - 1) / kEpExperts;
+  const int need = (T * k + kEpThreads - 1) / kEpThreads;
+#define MOEQ4_EP(P)                                                                           \
+  hipLaunchKernelGGL(permute_experts_kernel<P>, dim3(grid), dim3(kEpThreads), 0, s, idx, T, k, \
+                     E, offsets, sorted_tok, slot_row, shared_rows, bm, tiles, cap, tile_count)
+  if (need <= 1) MOEQ4_EP(1);
+  else if (need <= 2) MOEQ4_EP(2);
+  else if (need <= 4) MOEQ4_EP(4);
+  else if (need <= 8) MOEQ4_EP(8);
+  else if (need <= 16) MOEQ4_EP(16);
+  else MOEQ4_EP(32);
+#undef MOEQ4_EP
 }
 
 }  // namespace moeq4
