@@ -326,8 +326,9 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
 
 // Fewer tokens (D % 256 == 0): the fp32 matrix cores on R itself (v_mfma_f32_16x16x4_f32,
 // bf16 x widened exactly), so no split of R is needed.  Workgroup tile: 16 tokens x 32
-// experts; its eight wavefronts are two 16-expert tiles times four quarters of each
-// 256-K chunk, with two accumulators each, added through LDS at the end.  The chunk's R
+// experts; its sixteen wavefronts (four per SIMD, to hide the LDS and load latencies) are
+// two 16-expert tiles times eight 32-K parts of each 256-K chunk, with two accumulators
+// each, added through LDS at the end in a fixed order.  The chunk's R
 // rows (1 KB each) and x rows go through padded LDS rows with line-whole loads, one
 // chunk ahead in VGPRs.  In MFMA step s of a 16-K group, lane (m, q) supplies
 // k = 16 g + 4 q + s of token row m and of expert column m, so its operands of four
@@ -336,54 +337,56 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
 constexpr int kF32KC = 256;
 constexpr int kF32RRow = kF32KC * 4 + 16;  // padded LDS row of R, bytes
 constexpr int kF32XRow = kF32KC * 2 + 16;  // padded LDS row of x, bytes
-__global__ __launch_bounds__(512) void router_logits_f32_kernel(
+constexpr int kF32Threads = 1024;
+__global__ __launch_bounds__(kF32Threads) void router_logits_f32_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ R, float* __restrict__ L, int T, int D,
     int E, uint16_t* __restrict__ xprep) {
   __shared__ __attribute__((aligned(16))) unsigned char rs[2][32 * kF32RRow];
   __shared__ __attribute__((aligned(16))) unsigned char xsh[2][16 * kF32XRow];
-  __shared__ f32x4_t red[3][2][64];
+  __shared__ f32x4_t red[7][2][64];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int m = l & 15, q = l >> 4;
   const int tile = wave & 1, kq = wave >> 1;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 32;
   const int nch = D / kF32KC;
-  // this thread's pieces: R rows (tid / 64) + 8 i, 16-byte piece tid % 64; x row tid / 32,
-  // 16-byte piece tid % 32
-  const float* rsrc[4];
-  uint32_t rdst[4];
+  // this thread's pieces: R rows (tid / 64) + 16 i, 16-byte piece tid % 64; x row tid / 32
+  // (threads below 512), 16-byte piece tid % 32
+  const float* rsrc[2];
+  uint32_t rdst[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 6) + 8 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid >> 6) + 16 * i;
     rsrc[i] = R + (int64_t)min(e0 + row, E - 1) * D + 4 * (tid & 63);
     rdst[i] = (uint32_t)(row * kF32RRow + 16 * (tid & 63));
   }
-  const int xr = tid >> 5, xc = tid & 31;
-  const bool xv = t0 + xr < T;
+  const int xr = (tid >> 5) & 15, xc = tid & 31;
+  const bool xl = tid < 512;  // loads and stores an x piece
+  const bool xv = xl && t0 + xr < T;
   const uint16_t* xsrc = x + (int64_t)min(t0 + xr, T - 1) * D + 8 * xc;
   const uint32_t xdst = (uint32_t)(xr * kF32XRow + 16 * xc);
   const bool prep = xprep != nullptr && blockIdx.y == 0;
   // two register sets: chunk ch + 2 is loaded while ch is computed and ch + 1 is stored
   struct Piece {
-    u32x4_t r[4], x;
+    u32x4_t r[2], x;
   };
   auto load = [&](Piece& pc, int ch) __attribute__((always_inline)) {
     ch = min(ch, nch - 1);  // past the end: the last chunk again (never stored)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pc.r[i] = *(const u32x4_t*)(rsrc[i] + ch * kF32KC);
-    pc.x = *(const u32x4_t*)(xsrc + ch * kF32KC);
+    for (int i = 0; i < 2; ++i) pc.r[i] = *(const u32x4_t*)(rsrc[i] + ch * kF32KC);
+    if (xl) pc.x = *(const u32x4_t*)(xsrc + ch * kF32KC);
   };
   auto store = [&](const Piece& pc, int ch, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)(&rs[buf][rdst[i]]) = pc.r[i];
-    *(u32x4_t*)(&xsh[buf][xdst]) = pc.x;
+    for (int i = 0; i < 2; ++i) *(u32x4_t*)(&rs[buf][rdst[i]]) = pc.r[i];
+    if (xl) *(u32x4_t*)(&xsh[buf][xdst]) = pc.x;
     if (prep && xv) *(u32x4_t*)(xprep + (int64_t)(t0 + xr) * D + ch * kF32KC + 8 * xc) = interleave8(pc.x);
   };
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   auto compute = [&](int buf) __attribute__((always_inline)) {
-    const unsigned char* rb = &rs[buf][(16 * tile + m) * kF32RRow + kq * 256];
-    const unsigned char* xb = &xsh[buf][m * kF32XRow + kq * 128];
+    const unsigned char* rb = &rs[buf][(16 * tile + m) * kF32RRow + kq * 128];
+    const unsigned char* xb = &xsh[buf][m * kF32XRow + kq * 64];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < 2; ++g) {
       const f32x4_t rv = *(const f32x4_t*)(rb + (16 * g + 4 * q) * 4);
       const u32x2_t xw = *(const u32x2_t*)(xb + (16 * g + 4 * q) * 2);
       acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo_to_f32(xw[0]), rv[0], acc0, 0, 0, 0);
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(512) void router_logits_f32_kernel(
   const int e = e0 + 16 * tile + m;
   if (kq == 0 && e < E) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < 7; ++j) {
       const f32x4_t o = red[j][tile][l];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += o[i];
@@ -443,7 +446,8 @@ void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, in
                    uint16_t* xprep, hipStream_t s) {
   if (T < 2048 && D % kF32KC == 0) {
     dim3 grid((T + 15) / 16, (E + 31) / 32);
-    hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(512), 0, s, x, R, L, T, D, E, xprep);
+    hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(kF32Threads), 0, s, x, R, L, T, D, E,
+                       xprep);
     return;
   }
   launch_router_split(R, Rs, E, D, s);
