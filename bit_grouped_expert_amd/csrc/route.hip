@@ -442,8 +442,16 @@ __global__ __launch_bounds__(kF32Threads) void router_logits_f32_kernel(
   }
 }
 
+constexpr int kSmallTok = 16;  // the one-wavefront-per-expert kernel serves T <= 16
+static void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
+                                uint16_t* xprep, hipStream_t s);
+
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
                    uint16_t* xprep, hipStream_t s) {
+  if (T <= kSmallTok && D % 256 == 0) {
+    launch_router_small(x, R, L, T, D, E, xprep, s);
+    return;
+  }
   if (T < 2048 && D % kF32KC == 0) {
     dim3 grid((T + 15) / 16, (E + 31) / 32);
     hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(kF32Threads), 0, s, x, R, L, T, D, E,
@@ -695,6 +703,82 @@ void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
   else
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+}
+
+// ---------------------------------------------------------------------------- few tokens
+// T <= 16 (decode): one wavefront per expert, four per workgroup, so that R (E * D * 4
+// bytes, the bulk of the router's traffic) streams through every compute unit instead of
+// the few workgroups a 16-token tile would give.  Lane l takes k = 256 s + 4 l .. + 3 of
+// each 256-K step s: one 16-byte load of R and one 8-byte load of each token's x (TT
+// tokens, T rounded up; rows past T re-read the last row and are dropped), all of a step
+// issued before any is used (and a few steps at a time); the lane sums in fp32 in k order, then the wavefront sums in
+// a fixed DPP order.  The workgroups also write the prepared copy of x (runs of 8 columns
+// in the order 0,4,1,5,2,6,3,7, one zero row after the last token).
+template <int TT>
+__global__ __launch_bounds__(256) void router_logits_small_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ R, float* __restrict__ L, int T, int D,
+    int E, uint16_t* __restrict__ xprep) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wave;
+  if (xprep) {
+    const int pieces = (T + 1) * (D >> 3);
+    for (int pc = blockIdx.x * 256 + threadIdx.x; pc < pieces; pc += gridDim.x * 256) {
+      const int row = pc / (D >> 3), c8 = pc - row * (D >> 3);
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row < T) v = interleave8(*(const u32x4_t*)(x + (int64_t)row * D + 8 * c8));
+      *(u32x4_t*)(xprep + (int64_t)row * D + 8 * c8) = v;
+    }
+  }
+  if (e >= E) return;  // uniform per wavefront; no barriers
+  const float* r = R + (int64_t)e * D + 4 * lane;
+  const uint16_t* xr[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) xr[t] = x + (int64_t)min(t, T - 1) * D + 4 * lane;
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  constexpr int UN = TT <= 4 ? 4 : 2;  // steps whose loads are in flight together
+  for (int k0 = 0; k0 < D; k0 += 256 * UN) {
+    f32x4_t rv[UN];
+    u32x2_t xw[UN][TT];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int kk = min(k0 + 256 * u, D - 256);  // past the end: a valid step, not summed
+      rv[u] = *(const f32x4_t*)(r + kk);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) xw[u][t] = *(const u32x2_t*)(xr[t] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      if (k0 + 256 * u < D) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          acc[t] = fmaf(bf16lo_to_f32(xw[u][t][0]), rv[u][0], acc[t]);
+          acc[t] = fmaf(bf16hi_to_f32(xw[u][t][0]), rv[u][1], acc[t]);
+          acc[t] = fmaf(bf16lo_to_f32(xw[u][t][1]), rv[u][2], acc[t]);
+          acc[t] = fmaf(bf16hi_to_f32(xw[u][t][1]), rv[u][3], acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    if (t < T) {
+      const float v = wave_sum_f32(acc[t]);
+      if (lane == 0) L[(int64_t)t * E + e] = v;
+    }
+  }
+}
+
+static void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
+                                uint16_t* xprep, hipStream_t s) {
+  const dim3 grid((E + 3) / 4), block(256);
+  if (T <= 1)
+    hipLaunchKernelGGL(router_logits_small_kernel<1>, grid, block, 0, s, x, R, L, T, D, E, xprep);
+  else if (T <= 4)
+    hipLaunchKernelGGL(router_logits_small_kernel<4>, grid, block, 0, s, x, R, L, T, D, E, xprep);
+  else
+    hipLaunchKernelGGL(router_logits_small_kernel<16>, grid, block, 0, s, x, R, L, T, D, E, xprep);
 }
 
 }  // namespace moeq4
