@@ -350,35 +350,45 @@ constexpr int kEpPer = 32;      // pairs per thread
 constexpr int kEpExperts = 4;   // experts per workgroup
 constexpr int kEpMaxE = 1024;
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
-  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
-  return ((uint64_t)hi << 32) | lo;
+// Inclusive scan over the wavefront with DPP row shifts (within rows of 16 lanes), then
+// the row broadcasts of lanes 15 and 31.  Lanes a step does not update add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
 }
 
-// Exclusive scan of one uint64 per thread over a 256-thread block (sums wrap mod 2^64;
-// callers keep every 16- or 32-bit field below its width).  *total = the block's sum.
+// Exclusive scan of one uint64 per thread over a 256-thread block, as two independent
+// 32-bit scans of its halves (callers keep every 16- or 32-bit field below its width, so
+// no carry crosses them).  *total = the block's sum.  Every thread must call it.
 __device__ uint64_t block_exclusive_scan_u64_256(uint64_t v, uint64_t* total) {
-  __shared__ uint64_t wsum[kEpThreads / 64];
+  __shared__ uint32_t wsum[2 * (kEpThreads / 64)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t o = shfl_up_u64(incl, d);
-    if (lane >= d) incl += o;
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t ilo = wave_incl_scan_u32(lo), ihi = wave_incl_scan_u32(hi);
+  if (lane == 63) {
+    wsum[wave] = ilo;
+    wsum[kEpThreads / 64 + wave] = ihi;
   }
-  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint64_t base = 0, tot = 0;
+  uint32_t blo = 0, bhi = 0, tlo = 0, thi = 0;
 #pragma unroll
   for (int w = 0; w < kEpThreads / 64; ++w) {
-    const uint64_t sv = wsum[w];
-    if (w < wave) base += sv;
-    tot += sv;
+    const uint32_t sl = wsum[w], sh = wsum[kEpThreads / 64 + w];
+    if (w < wave) {
+      blo += sl;
+      bhi += sh;
+    }
+    tlo += sl;
+    thi += sh;
   }
   __syncthreads();  // wsum may be reused by the next call
-  *total = tot;
-  return base + incl - v;
+  *total = ((uint64_t)thi << 32) | tlo;
+  return ((uint64_t)(bhi + ihi - hi) << 32) | (uint64_t)(blo + ilo - lo);
 }
 
 // PER: pairs per thread, a power of two with 256 * PER >= T * k (fixed at compile time,
@@ -471,6 +481,7 @@ __global__ __launch_bounds__(kEpThreads) void permute_experts_kernel(
   }
   uint64_t unused;
   uint64_t run = block_exclusive_scan_u64_256(mine, &unused);
+  int tok = f0 / k, slot = f0 - (f0 / k) * k;  // token and slot of pair f0 + j, stepped
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (f0 + j < n) {
@@ -478,12 +489,16 @@ __global__ __launch_bounds__(kEpThreads) void permute_experts_kernel(
       if (d >= 0 && d < kEpExperts && e < E) {
         int row = offl[e] + (int)((run >> (16 * d)) & 0xFFFFu);
         run += 1ull << (16 * d);
-        if (row >= 0 && row < n) sorted_tok[row] = (f0 + j) / k;  // always, for consistent counts
+        if (row >= 0 && row < n) sorted_tok[row] = tok;  // always, for consistent counts
         else row = -1;
         slot_row[f0 + j] = row;
       } else if ((e < 0 || e >= E) && blockIdx.x == 0) {
         slot_row[f0 + j] = -1;
       }
+    }
+    if (++slot == k) {
+      slot = 0;
+      ++tok;
     }
   }
 
