@@ -36,6 +36,8 @@
 // product (a quarter of the bf16 matrix time), the dependent chain of each fragment's
 // two MFMAs and its fold, and four rounds of tiles for 3.05 rounds of work account for
 // most of it.
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 #include "q4_stream.h"
@@ -57,6 +59,15 @@ struct WideLds {
   unsigned char* stg;
 };
 
+// blocks of 256 weight rows per unit of a last round: enough for four 256-K stages, and a
+// divisor of the tile's NB blocks
+__host__ __device__ inline int wide_unit_blocks(int NB, int NK) {
+  int ub = NK >= 4 ? 1 : (4 + NK - 1) / NK;
+  if (ub > NB) ub = NB;
+  while (NB % ub) --ub;
+  return ub;
+}
+
 template <bool SWIGLU, int GS>
 __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& lds) {
   constexpr int D = 2;  // weight register sets: the next stage's in flight
@@ -65,15 +76,35 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   const int m = l & 15, q = l >> 4;
   const int N = p.N, K = p.K, KW = K >> 3, KG = K >> 6, NK = K / WKS;
   const int NB = SWIGLU ? (N >> 1) / 128 : N / 256;
-  const int UT = NB * NK;  // stages of the whole tile: block blk, stage st at blk * NK + st
 
-  // ---- this workgroup's tile: XCD b % 8 takes a contiguous run of tiles
+  // ---- this workgroup's work: XCD b % 8 takes a contiguous run of `per` tiles, one
+  // workgroup per tile in order (the hardware starts the next one wherever a compute unit
+  // of the XCD frees up).  With xcd_cus set, the tiles of the XCD's last, partial round
+  // (those past its whole rounds of xcd_cus tiles) get one workgroup per unit of UB
+  // blocks of 256 weight rows instead (at least four stages each), so that this round
+  // spreads over the compute units.
   const int cnt = *p.tile_count;
   const int per = (cnt + 7) >> 3;
   const int jx = blockIdx.x >> 3;
-  if (jx >= per) return;  // uniform, before any barrier
-  const int tile = (blockIdx.x & 7) * per + jx;
+  const int UB = wide_unit_blocks(NB, NK), NUT = NB / UB;  // blocks per unit, units per tile
+  int tile, blk0 = 0, nblk = NB;
+  if (p.xcd_cus > 0) {
+    const int full = per / p.xcd_cus * p.xcd_cus;  // tiles in whole rounds
+    if (jx < full) {
+      tile = (blockIdx.x & 7) * per + jx;
+    } else {
+      const int u = jx - full;
+      if (u >= (per - full) * NUT) return;  // uniform, before any barrier
+      tile = (blockIdx.x & 7) * per + full + u / NUT;
+      blk0 = (u - (u / NUT) * NUT) * UB;
+      nblk = UB;
+    }
+  } else {
+    if (jx >= per) return;  // uniform, before any barrier
+    tile = (blockIdx.x & 7) * per + jx;
+  }
   if (tile >= cnt) return;
+  const int UT = nblk * NK;  // stages of this workgroup: block blk0 + v / NK, stage v % NK
   const int4 tt = p.tiles[tile];
   const int grp = __builtin_amdgcn_readfirstlane(tt.x);
   const int row0 = __builtin_amdgcn_readfirstlane(tt.y);
@@ -107,7 +138,7 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   int pf_v = 0;
   auto pf_load = [&](StageW& w) __attribute__((always_inline)) {
     const int v = min(pf_v, UT - 1);
-    const int blk = v / NK, st = v - blk * NK;
+    const int vb = v / NK, st = v - vb * NK, blk = blk0 + vb;
     int n0, n1;
     if (SWIGLU) {
       const int u = 8 * blk + wave;
@@ -301,13 +332,13 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   // stage its outputs, then the accumulators start over.
   auto step = [&](int v, const unsigned char* cur_a, unsigned char* next_a, StageW& cur,
                   StageW& fresh) __attribute__((always_inline)) {
-    const int blk = v / NK, st = v - blk * NK;
+    const int vb = v / NK, st = v - vb * NK, blk = blk0 + vb;
     const int vn = v + 1 < UT ? v + 1 : v;  // the last stage loads itself again
     issue_a(vn - (vn / NK) * NK, next_a);
     pf_load(fresh);
     float cbq[2];
     compute(cur, cur_a, cbq);
-    if (blk == 0) row_sums(st, cur_a);
+    if (vb == 0) row_sums(st, cur_a);  // X during the first block of this workgroup
     wait_vmcnt0();
     lds_barrier();
     bias_term(st, cbq);
@@ -342,9 +373,23 @@ __global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
 }
 
 template <bool SWIGLU>
-void launch_w(const TiledParams& p, int64_t n_tiles_bound, hipStream_t s) {
-  const int64_t grid = ((n_tiles_bound > 0 ? n_tiles_bound : 1) + 7) / 8 * 8;
-  hipLaunchKernelGGL((q4_wide_kernel<SWIGLU>), dim3((unsigned)grid), dim3(512), 0, s, p);
+void launch_w(TiledParams p, int64_t n_tiles_bound, hipStream_t s) {
+  const int64_t bound = n_tiles_bound > 0 ? n_tiles_bound : 1;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 0;
+  const int xc = ncu / 8;
+  const int NB = SWIGLU ? (p.N >> 1) / 128 : p.N / 256;
+  const int NUT = NB / wide_unit_blocks(NB, p.K / WKS);  // units per tile of a last round
+  // workgroups per XCD: at most per + (xcd_cus - 1) (NUT - 1) for any tile count up to
+  // the bound (per <= ceil(bound / 8): whole rounds, then at most xcd_cus - 1 tiles of NUT)
+  const int64_t per_b = (bound + 7) / 8;
+  const char* env = getenv("MOEQ4_WIDE_SPLIT");  // "0": one workgroup per tile throughout
+  const bool split = !(env && env[0] == '0');
+  p.xcd_cus = split && xc >= 1 && per_b >= xc ? xc : 0;
+  const int64_t per_xcd = p.xcd_cus ? per_b + (int64_t)(xc - 1) * (NUT - 1) : per_b;
+  hipLaunchKernelGGL((q4_wide_kernel<SWIGLU>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
 }
 
 }  // namespace

@@ -176,6 +176,7 @@ struct TiledParams {
   int32_t c_perm;
   const int4* tiles;
   const int32_t* tile_count;
+  int32_t xcd_cus;  // wide engine: compute units per XCD (set by launch_wide; 0: one tile each)
 };
 bool tiled_supported(int N, int K, bool swiglu, int a_rows);
 void launch_tiled(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
