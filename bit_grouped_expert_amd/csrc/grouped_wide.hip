@@ -31,13 +31,14 @@
 // The tiles of an XCD's last, partial round go to one workgroup per unit of one or two
 // blocks instead of one per tile, so that this round is spread over the XCD.
 //
-// Measured at 8192 tokens it is no faster than the resident engine (gate_up 682 us):
-// timing variants put a full tile near 4 us per stage against 1.7 us of bf16 matrix
-// work; without any global load in the loop it still takes 514 us, and dropping the
-// fold, the unpacking or the LDS activation reads each changes little.  The fp32 bias
-// product (a quarter of the bf16 matrix time), the dependent chain of each fragment's
-// two MFMAs and its fold, and four rounds of tiles for 3.05 rounds of work account for
-// most of it.
+// Measured at 8192 tokens (uniform routing) gate_up takes about 566 us against 643 us
+// on the resident engine.  Hardware counters put the matrix cores at 29% busy (bf16
+// and the fp32 bias product together) and the cycles in which vector and matrix
+// instructions execute together at about 2%: the two wavefronts of a SIMD go through
+// their operand, MFMA and fold phases at the same time, so the folds and the unpacking
+// add to the matrix time instead of hiding under it.  Timing variants agree: without
+// any global load in the loop it still takes most of its time, and dropping the fold,
+// the unpacking or the LDS activation reads alone changes little.
 #include <stdlib.h>
 
 #include "common.h"
