@@ -615,20 +615,50 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
 #pragma unroll
         for (int j = 0; j < 4; ++j) Rr[j] = R + (int64_t)(j < nb ? ce[j] : ce[0]) * D;
         double sj[4] = {0.0, 0.0, 0.0, 0.0};
-        constexpr int UN = MAXC >= 16 ? 2 : 8;  // steps in flight (registers permitting)
-        for (int d0 = 0; d0 < D; d0 += 64 * UN) {
-          float xv[UN], rv[UN][4];
+        if constexpr (MAXC >= 16) {
+          // lane l takes d = 64 s + l of step s, two steps in flight (registers permitting)
+          constexpr int UN = 2;
+          for (int d0 = 0; d0 < D; d0 += 64 * UN) {
+            float xv[UN], rv[UN][4];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+              const int d = min(d0 + 64 * u + lane, D - 1);
+              xv[u] = d0 + 64 * u + lane < D ? bf16lo_to_f32(xt[d]) : 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) rv[u][j] = Rr[j][d];
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sj[j] += (double)xv[u] * (double)rv[u][j];
+          }
+        } else {
+        // lane l takes d = 256 s + 4 l .. 4 l + 3 of step s (D % 64 == 0: a step's four d
+        // are all in range or all out), 16-byte loads of each row, four steps in flight
+        // (half the dependent rounds of single-element loads at the same registers per d)
+        constexpr int UN = 4;
+        for (int d0 = 0; d0 < D; d0 += 256 * UN) {
+          u32x2_t xv[UN];
+          f32x4_t rv[UN][4];
 #pragma unroll
           for (int u = 0; u < UN; ++u) {
-            const int d = min(d0 + 64 * u + lane, D - 1);
-            xv[u] = d0 + 64 * u + lane < D ? bf16lo_to_f32(xt[d]) : 0.f;
+            const int dd = d0 + 256 * u + 4 * lane;
+            const int d = dd < D ? dd : D - 4;
+            xv[u] = *(const u32x2_t*)(xt + d);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) rv[u][j] = Rr[j][d];
+            for (int j = 0; j < 4; ++j) rv[u][j] = *(const f32x4_t*)(Rr[j] + d);
+            if (dd >= D) xv[u] = u32x2_t{0u, 0u};
           }
 #pragma unroll
-          for (int u = 0; u < UN; ++u)
+          for (int u = 0; u < UN; ++u) {
+            const float xf[4] = {bf16lo_to_f32(xv[u][0]), bf16hi_to_f32(xv[u][0]),
+                                 bf16lo_to_f32(xv[u][1]), bf16hi_to_f32(xv[u][1])};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sj[j] += (double)xv[u] * (double)rv[u][j];
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sj[j] += (double)xf[c] * (double)rv[u][j][c];
+          }
+        }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -419,10 +419,11 @@ def test_layer_forward_no_shared(torch_cuda):
 @pytest.mark.parametrize("shape", [(33, 128, 40, 32, 64), (40, 64, 1000, 4, 64), (300, 192, 8, 1, 192),
                                    (1500, 320, 4, 2, 192), (1500, 256, 4, 2, 128),
                                    (77, 384, 24, 3, 256), (5, 128, 16, 4, 128),
-                                   (300, 512, 24, 3, 256), (40, 1024, 64, 4, 512)])
+                                   (300, 512, 24, 3, 256), (40, 1024, 64, 4, 512),
+                                   (64, 64, 1024, 16, 64)])
 def test_layer_forward_odd_shapes(torch_cuda, shape, engine):
-    """Wide top-k (k = 32), many experts (E = 1000), K % 128 == 64 (D = F = 192), a single expert
-    per token."""
+    """Wide top-k (k = 32), many experts (E = 1000, and E = 1024, the most the interface takes,
+    with 613 of them touched), K % 128 == 64 (D = F = 192), a single expert per token."""
     T, D, E, k, F = shape
     cfg = wl.MoEConfig("odd", T, D, E, k, F)
     x, router = wl.make_activations(cfg, 5)
