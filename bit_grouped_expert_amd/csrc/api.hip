@@ -249,13 +249,20 @@ moe_status moe_route_ex(const moe_shape* shape, const uint16_t* x, const float* 
   return route_impl(shape, x, router_w, topk_idx, topk_w, ws, ws_bytes, stream, refine_gap);
 }
 
+// Chunked histogram, scan and scatter; with tiles set the scan launch also writes the
+// tile map (bm rows per tile over rows_total rows).
 static moe_status permute_impl(const moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
                                int32_t* sorted_tok, int32_t* slot_row, int32_t* chunk_cnt,
-                               int shared_rows, hipStream_t stream) {
+                               int shared_rows, hipStream_t stream, int4* tiles = nullptr,
+                               int32_t* tile_count = nullptr, int rows_total = 0, int bm = 1) {
   const int T = shape->T, E = shape->n_experts, k = shape->top_k;
   const int nch = n_chunks(T);
   launch_count(topk_idx, T, k, E, chunk_cnt, stream);
-  launch_scan(chunk_cnt, nch, E, offsets, shared_rows, stream);
+  if (tiles)
+    launch_scan_tiles(chunk_cnt, nch, E, offsets, shared_rows, rows_total, bm, tiles, tile_count,
+                      stream);
+  else
+    launch_scan(chunk_cnt, nch, E, offsets, shared_rows, stream);
   launch_scatter(topk_idx, T, k, E, chunk_cnt, offsets, sorted_tok, slot_row,
                  shared_rows >= 0 ? T * k : -1, stream);
   return MOE_OK;
@@ -493,8 +500,7 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
                          plan.bm, tiles, tile_count, stream);
   } else {
     permute_impl(shape, idx, offsets, sorted_tok, slot_row, at<int32_t>(ws, L.chunk_cnt),
-                 has_shared ? T : -1, stream);
-    launch_build_tiles(offsets, n_groups, rows, plan.bm, tiles, tile_count, stream);
+                 has_shared ? T : -1, stream, tiles, tile_count, (int)rows, plan.bm);
   }
   if (plan.eng == ENG_STREAM) launch_prep(x, T, D, at<uint16_t>(ws, L.xprep), at<float4>(ws, L.xc_x), stream);
   else if (plan.eng == ENG_GROUPED) launch_row_group_sums(x, T, D, xsum_x, stream);

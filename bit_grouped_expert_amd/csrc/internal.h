@@ -31,6 +31,10 @@ void launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int s
 void launch_scatter(const int32_t* idx, int T, int k, int E, const int32_t* chunk_base,
                     const int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, int shared_base,
                     hipStream_t s);
+// launch_scan followed, in the same single-workgroup launch, by the tile map of the E
+// routed groups (+ the shared group when shared_rows >= 0) over rows_total rows
+void launch_scan_tiles(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
+                       int rows_total, int bm, int4* tiles, int32_t* tile_count, hipStream_t s);
 
 // ---------------------------------------------------------------- grouped GEMM
 struct Q4Ptrs {

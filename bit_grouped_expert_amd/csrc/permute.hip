@@ -78,13 +78,24 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return base + incl - v;
 }
 
+__device__ void write_tiles(const int32_t* offs, int n_groups, int rows_total, int bm,
+                            int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count,
+                            int* tab);
+
 // ---------------------------------------------------------------------------- scan
 // One workgroup of 1024 threads.  chunk_cnt [nchunks, E] is replaced by each
 // chunk's exclusive base per expert; offsets[0..E] is the exclusive scan of the
 // expert totals; if shared_rows >= 0, offsets[E+1] = offsets[E] + shared_rows.
+// With tiles set, the same workgroup then writes the tile map of the E routed groups
+// (and the shared one when shared_rows >= 0) from the offsets it holds, as
+// build_tiles_kernel would from the written ones.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ chunk_cnt, int nchunks,
                                                     int E, int32_t* __restrict__ offsets,
-                                                    int shared_rows) {
+                                                    int shared_rows, int rows_total, int bm,
+                                                    int4* __restrict__ tiles, int cap,
+                                                    int32_t* __restrict__ tile_count) {
+  __shared__ int soff[kMaxTileGroups + 1];
+  __shared__ int tab[3 * (kMaxTileGroups + 1)];
   const int e = threadIdx.x;
   int running = 0;
   if (e < E) {
@@ -112,12 +123,29 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ chunk_
     offsets[E] = total;
     if (shared_rows >= 0) offsets[E + 1] = total + shared_rows;
   }
+  if (tiles) {  // uniform: a kernel argument
+    if (e < E) soff[e] = excl;
+    if (threadIdx.x == 0) {
+      soff[E] = total;
+      if (shared_rows >= 0) soff[E + 1] = total + shared_rows;
+    }
+    // write_tiles starts with a barrier, after which soff is complete
+    write_tiles(soff, shared_rows >= 0 ? E + 1 : E, rows_total, bm, tiles, cap, tile_count, tab);
+  }
 }
 
 void launch_scan(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
                  hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_cnt, nchunks, E, offsets,
-                     shared_rows);
+                     shared_rows, 0, 1, nullptr, 0, nullptr);
+}
+
+void launch_scan_tiles(int32_t* chunk_cnt, int nchunks, int E, int32_t* offsets, int shared_rows,
+                       int rows_total, int bm, int4* tiles, int32_t* tile_count, hipStream_t s) {
+  const int n_groups = shared_rows >= 0 ? E + 1 : E;
+  const int cap = (int)max_tiles(rows_total, n_groups, bm);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_cnt, nchunks, E, offsets,
+                     shared_rows, rows_total, bm, tiles, cap, tile_count);
 }
 
 // ---------------------------------------------------------------------------- scatter

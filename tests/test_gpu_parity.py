@@ -420,10 +420,12 @@ def test_layer_forward_no_shared(torch_cuda):
                                    (1500, 320, 4, 2, 192), (1500, 256, 4, 2, 128),
                                    (77, 384, 24, 3, 256), (5, 128, 16, 4, 128),
                                    (300, 512, 24, 3, 256), (40, 1024, 64, 4, 512),
-                                   (64, 64, 1024, 16, 64)])
+                                   (64, 64, 1024, 16, 64), (1100, 256, 64, 8, 128)])
 def test_layer_forward_odd_shapes(torch_cuda, shape, engine):
     """Wide top-k (k = 32), many experts (E = 1000, and E = 1024, the most the interface takes,
-    with 613 of them touched), K % 128 == 64 (D = F = 192), a single expert per token."""
+    with 613 of them touched), K % 128 == 64 (D = F = 192), a single expert per token, and
+    T * k > 8192 with T > 1024 (the chunked histogram, scan and scatter with the tile map
+    written by the scan launch), every output element checked."""
     T, D, E, k, F = shape
     cfg = wl.MoEConfig("odd", T, D, E, k, F)
     x, router = wl.make_activations(cfg, 5)
