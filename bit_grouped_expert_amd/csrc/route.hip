@@ -286,9 +286,9 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
   __syncthreads();
   for (int ch = 0; ch < nch; ++ch) {
     const int buf = ch & 1;
-    const bool more = ch + 1 < nch;
-    const int chn = more ? ch + 1 : ch;  // the last chunk loads itself again
+    const int chn = ch + 1 < nch ? ch + 1 : ch;  // the last chunk loads itself again
     load_x(xr, chn);
+    __builtin_amdgcn_sched_barrier(0);  // issued a chunk ahead of their store, not sunk to it
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4_t xa[4];
@@ -301,12 +301,15 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
         a1[f] = mfma16x16x32(xa[f], rv[s][1], a1[f]);
         a2[f] = mfma16x16x32(xa[f], rv[s][2], a2[f]);
       }
+      // the step's fragments reloaded here, a whole chunk before their next use (left to
+      // itself the scheduler sinks all of a chunk's reloads to its end)
       load_r(rv[s], 8 * chn + s);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      store_x(xr, chn, buf ^ 1);
-      __syncthreads();
-    }
+    // unconditional (after the last chunk it stores that chunk again into the unused
+    // buffer), so that the compiler does not sink the loads of xr into a branch here
+    store_x(xr, chn, buf ^ 1);
+    __syncthreads();
   }
   if (xprep && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) {
     // the zero row after the last token
