@@ -9,7 +9,14 @@
 //
 // Arithmetic: as in the resident-tile engine (exact up to fp32 rounding): per 64-wide
 // group, P' = sum x (128 + q) on the matrix cores from zero, acc += s P', and the bias
-// term (b - 128 s) X as an fp32 matrix-core product with the stage's four groups as k.
+// term sum_g (b - 128 s) X.  Where K >= 1024 the bias term is formed once per block of
+// weight rows, as bf16 matrix-core products with all 32 groups as k: b X and s X with
+// X split exactly into three bf16 pieces (b and s are bf16 already, so every product is
+// exact), then acc += b X - 128 (s X).  Timing the engine without any bias term put the
+// per-stage fp32 product (v_mfma_f32_16x16x4_f32, the stage's four groups as k, 32
+// cycles per 16x16 block) at about 18% of gate_up at 8192 tokens.  With fewer groups
+// (the down GEMM, K = 512) the 32-wide k is mostly zeros and the per-stage fp32
+// product is kept.
 //
 // Work decomposition.  One workgroup per tile of up to 128 rows of one group (eight
 // 16-row fragments); it walks every block of 256 weight rows (with SwiGLU: 128 gate
@@ -31,7 +38,7 @@
 // The tiles of an XCD's last, partial round go to one workgroup per unit of one or two
 // blocks instead of one per tile, so that this round is spread over the XCD.
 //
-// Measured at 8192 tokens (uniform routing) gate_up takes about 566 us against 643 us
+// Measured at 8192 tokens (uniform routing) gate_up takes about 545 us against 643 us
 // on the resident engine.  Hardware counters put the matrix cores at 29% busy (bf16
 // and the fp32 bias product together) and the cycles in which vector and matrix
 // instructions execute together at about 2%: the two wavefronts of a SIMD go through
@@ -52,13 +59,16 @@ namespace {
 constexpr int WBM = kWideBM;                 // rows per tile
 constexpr int WKS = 256;                     // K per stage (four groups)
 constexpr int A_BUF = (WBM / 16) * 32 * 256; // [fragment 8][16-byte chunk 32][row 16]: 64 KB
-constexpr int XS_FLOATS = (kWideMaxK / 64) * WBM;  // X, fp32 [K / 64][128 rows]
+constexpr int XG = kWideMaxK / 64;           // 64-wide groups of the largest K (32)
+constexpr int XP_PIECE = WBM * XG * 2;       // one bf16 piece of X: [128 rows][32 groups]
+constexpr int XP_BYTES = 3 * XP_PIECE;       // X = hi + mid + lo, exactly: 24 KB
 constexpr int STG_BYTES = 8 * 1024;          // epilogue staging, 1 KB per wavefront
-static_assert(2 * A_BUF + 4 * XS_FLOATS + STG_BYTES <= 160 * 1024, "LDS budget");
+static_assert(XG == 32, "one 16x16x32 MFMA covers every group of the largest K");
+static_assert(2 * A_BUF + XP_BYTES + STG_BYTES <= 160 * 1024, "LDS budget");
 
 struct WideLds {
   unsigned char* a[2];
-  float* xs;
+  unsigned char* xp;
   unsigned char* stg;
 };
 
@@ -71,7 +81,9 @@ __host__ __device__ inline int wide_unit_blocks(int NB, int NK) {
   return ub;
 }
 
-template <bool SWIGLU, int GS>
+// BB: the bias term once per block as bf16 products over all groups (K >= 1024), else
+// per stage as an fp32 product over the stage's four groups.
+template <bool SWIGLU, int GS, bool BB>
 __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& lds) {
   constexpr int D = 2;  // weight register sets: the next stage's in flight
   const int tid = threadIdx.x, l = tid & 63;
@@ -194,16 +206,18 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 
   // One 256-K stage in two 128-K halves (MFMA steps 2 (g ^ GS), 2 (g ^ GS) + 1 of a
   // half take its scale group g, as in the resident engine): per row fragment, P' of
-  // both weight fragments and both groups from zero, then acc += s P'.  cbq: the
-  // lane's (b - 128 s) of group q of the stage, for the bias term.
+  // both weight fragments and both groups from zero, then acc += s P'.  cbq (per-stage
+  // bias only): the lane's (b - 128 s) of group q of the stage.
   auto compute = [&](const StageW& w, const unsigned char* abuf, float* cbq) __attribute__((always_inline)) {
+    if constexpr (!BB) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t sw = (q & 2) ? w.s[j][1] : w.s[j][0];
-      const uint32_t bw = (q & 2) ? w.b[j][1] : w.b[j][0];
-      const float sq = (q & 1) ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
-      const float bq = (q & 1) ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
-      cbq[j] = fmaf(-128.f, sq, bq);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t sw = (q & 2) ? w.s[j][1] : w.s[j][0];
+        const uint32_t bw = (q & 2) ? w.b[j][1] : w.b[j][0];
+        const float sq = (q & 1) ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
+        const float bq = (q & 1) ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
+        cbq[j] = fmaf(-128.f, sq, bq);
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -258,10 +272,11 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
       }
     }
   };
-  // X[group][row] of this wavefront's fragment for the stage's four groups: the product
-  // of the group's two 32-K activation fragments with a fragment of ones, written by
-  // the lanes of column 0
-  float* xs = lds.xs;
+  // X[row][group] of this wavefront's fragment for the stage's four groups: the product
+  // of the group's two 32-K activation fragments with a fragment of ones (lanes of column
+  // 0 hold it), stored as three bf16 pieces whose sum is X exactly (each takes the top
+  // eight significant bits of what the previous ones left)
+  unsigned char* xp = lds.xp;
   auto row_sums = [&](int st, const unsigned char* abuf) __attribute__((always_inline)) {
     if (wave < nfv) {
       const unsigned char* af = abuf + wave * 8192 + 16 * m;
@@ -270,14 +285,59 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
         const u32x4_t a0 = *(const u32x4_t*)(af + (8 * g4 + q) * 256);
         const u32x4_t a1 = *(const u32x4_t*)(af + (8 * g4 + 4 + q) * 256);
         const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
-        if (m == 0) *(f32x4_t*)(xs + (4 * st + g4) * WBM + 16 * wave + 4 * q) = X;
+        if (!BB && m == 0)
+          *(f32x4_t*)((float*)xp + (4 * st + g4) * WBM + 16 * wave + 4 * q) = X;  // [group][row]
+        if (BB && m == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t hi = __float_as_uint(X[i]) & 0xFFFF0000u;
+            const float r1 = X[i] - __uint_as_float(hi);
+            const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+            const float r2 = r1 - __uint_as_float(mid);
+            const uint32_t lo = __float_as_uint(r2) & 0xFFFF0000u;
+            const int off = (16 * wave + 4 * q + i) * (2 * XG) + 2 * (4 * st + g4);
+            *(uint16_t*)(xp + off) = (uint16_t)(hi >> 16);
+            *(uint16_t*)(xp + XP_PIECE + off) = (uint16_t)(mid >> 16);
+            *(uint16_t*)(xp + 2 * XP_PIECE + off) = (uint16_t)(lo >> 16);
+          }
+        }
       }
     }
   };
-  // acc += (b - 128 s) X over the stage's four groups (v_mfma_f32_16x16x4_f32: lane l
-  // gives A[row l % 16][k = l / 16] and B[k = l / 16][column l % 16], k = group)
+  // The bias term of a finished block, sum over groups of (b - 128 s) X, exactly up to
+  // fp32 rounding: b X and s X as bf16 products with the groups as k (v_mfma_f32_16x16x32:
+  // lane (m, q) gives X of row m and groups 8q .. 8q+7, lane (n, q) b or s of column n and
+  // the same groups), over the three pieces of X; then acc += b X - 128 (s X).  sb: this
+  // lane's s and b words of groups 8q .. 8q+7, captured from the stages as they passed.
+  u32x4_t cs[2], cb[2];  // [weight fragment]: s, b of groups 8q .. 8q+7 (zero past K)
+  auto clear_sb = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cs[j] = u32x4_t{0u, 0u, 0u, 0u};
+      cb[j] = cs[j];
+    }
+  };
+  clear_sb();
+  auto capture_sb = [&](int st, const StageW& w) __attribute__((always_inline)) {
+    const bool lo_half = (st >> 1) == q && (st & 1) == 0;  // groups 8q .. 8q+3
+    const bool hi_half = (st >> 1) == q && (st & 1) == 1;  // groups 8q+4 .. 8q+7
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cs[j][0] = lo_half ? w.s[j][0] : cs[j][0];
+      cs[j][1] = lo_half ? w.s[j][1] : cs[j][1];
+      cs[j][2] = hi_half ? w.s[j][0] : cs[j][2];
+      cs[j][3] = hi_half ? w.s[j][1] : cs[j][3];
+      cb[j][0] = lo_half ? w.b[j][0] : cb[j][0];
+      cb[j][1] = lo_half ? w.b[j][1] : cb[j][1];
+      cb[j][2] = hi_half ? w.b[j][0] : cb[j][2];
+      cb[j][3] = hi_half ? w.b[j][1] : cb[j][3];
+    }
+  };
+  // Per stage (without BB): acc += (b - 128 s) X over the stage's four groups
+  // (v_mfma_f32_16x16x4_f32: lane l gives A[row l % 16][k = l / 16] and B[k = l / 16]
+  // [column l % 16], k = group), X fp32 [group][row] in the same LDS.
   auto bias_term = [&](int st, const float* cbq) __attribute__((always_inline)) {
-    const float* xg = xs + (4 * st + q) * WBM + m;
+    const float* xg = (const float*)xp + (4 * st + q) * WBM + m;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f < nfv) {
@@ -285,6 +345,24 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, cbq[j], acc[f][j], 0, 0, 0);
+      }
+    }
+  };
+  auto bias_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f < nfv) {
+        const unsigned char* xr = xp + (16 * f + m) * (2 * XG) + 16 * q;
+        const u32x4_t x0 = *(const u32x4_t*)(xr);
+        const u32x4_t x1 = *(const u32x4_t*)(xr + XP_PIECE);
+        const u32x4_t x2 = *(const u32x4_t*)(xr + 2 * XP_PIECE);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4_t sx = mfma16x16x32(x2, cs[j], mfma16x16x32(x1, cs[j], mfma16x16x32(x0, cs[j], zero)));
+          acc[f][j] = mfma16x16x32(x2, cb[j], mfma16x16x32(x1, cb[j], mfma16x16x32(x0, cb[j], acc[f][j])));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+        }
       }
     }
   };
@@ -321,7 +399,9 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
     }
   };
 
-  // ---- prologue: stage 0's activations and weights
+  // ---- prologue: the pieces of X zeroed (groups past K stay zero), stage 0's
+  // activations and weights
+  for (int o = 16 * tid; o < XP_BYTES; o += 16 * 512) *(u32x4_t*)(xp + o) = u32x4_t{0u, 0u, 0u, 0u};
   StageW W[D];
   issue_a(0, lds.a[0]);
   pf_load(W[0]);
@@ -341,13 +421,16 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
     pf_load(fresh);
     float cbq[2];
     compute(cur, cur_a, cbq);
+    if (BB) capture_sb(st, cur);
     if (vb == 0) row_sums(st, cur_a);  // X during the first block of this workgroup
     wait_vmcnt0();
     lds_barrier();
-    bias_term(st, cbq);
-    if (st == NK - 1) {
+    if (!BB) bias_term(st, cbq);
+    if (st == NK - 1) {  // with BB: X of every group is in LDS since the first block's end
+      if (BB) bias_block();
       epilogue(blk);
       reset();
+      if (BB) clear_sb();
     }
   };
   int v = 0;
@@ -360,19 +443,19 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 
 // GS: scale group of MFMA steps 0 and 1 after the word swaps, read off the swapped
 // word numbers on entry (both orders compiled).
-template <bool SWIGLU>
+template <bool SWIGLU, bool BB>
 __global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char a0[A_BUF];
   __shared__ __attribute__((aligned(16))) unsigned char a1[A_BUF];
-  __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
+  __shared__ __attribute__((aligned(16))) unsigned char xp[XP_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char stg[STG_BYTES];
-  const WideLds lds{{a0, a1}, xs, stg};
+  const WideLds lds{{a0, a1}, xp, stg};
   const int l = threadIdx.x & 63;
   const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
                                                   false, false);
   const int gs = __builtin_amdgcn_readfirstlane((int)(r[0] >> 3));
-  if (gs) wide_body<SWIGLU, 1>(p, lds);
-  else wide_body<SWIGLU, 0>(p, lds);
+  if (gs) wide_body<SWIGLU, 1, BB>(p, lds);
+  else wide_body<SWIGLU, 0, BB>(p, lds);
 }
 
 template <bool SWIGLU>
@@ -392,7 +475,11 @@ void launch_w(TiledParams p, int64_t n_tiles_bound, hipStream_t s) {
   const bool split = !(env && env[0] == '0');
   p.xcd_cus = split && xc >= 1 && per_b >= xc ? xc : 0;
   const int64_t per_xcd = p.xcd_cus ? per_b + (int64_t)(xc - 1) * (NUT - 1) : per_b;
-  hipLaunchKernelGGL((q4_wide_kernel<SWIGLU>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
+  // the bias once per block pays where a block has at least four stages (16 groups)
+  if (p.K >= 4 * WKS)
+    hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, true>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, false>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
 }
 
 }  // namespace
