@@ -12,11 +12,11 @@
 // term sum_g (b - 128 s) X.  Where K >= 1024 the bias term is formed once per block of
 // weight rows, as bf16 matrix-core products with all 32 groups as k: b X and s X with
 // X split exactly into three bf16 pieces (b and s are bf16 already, so every product is
-// exact), then acc += b X - 128 (s X).  Timing the engine without any bias term put the
-// per-stage fp32 product (v_mfma_f32_16x16x4_f32, the stage's four groups as k, 32
-// cycles per 16x16 block) at about 18% of gate_up at 8192 tokens.  With fewer groups
-// (the down GEMM, K = 512) the 32-wide k is mostly zeros and the per-stage fp32
-// product is kept.
+// exact), then acc += b X - 128 (s X).  Where K <= 512 (the down GEMM) the three pieces
+// of X sit side by side in the 32-wide k (3 x 8 groups), so b X and s X are one MFMA
+// each.  In between (K = 768) the bias stays a per-stage fp32 product
+// (v_mfma_f32_16x16x4_f32, the stage's four groups as k); timing the engine without any
+// bias term put that product at about 18% of gate_up and 14% of down at 8192 tokens.
 //
 // Work decomposition.  One workgroup per tile of up to 128 rows of one group (eight
 // 16-row fragments); it walks every block of 256 weight rows (with SwiGLU: 128 gate
@@ -81,10 +81,13 @@ __host__ __device__ inline int wide_unit_blocks(int NB, int NK) {
   return ub;
 }
 
-// BB: the bias term once per block as bf16 products over all groups (K >= 1024), else
-// per stage as an fp32 product over the stage's four groups.
-template <bool SWIGLU, int GS, bool BB>
+// BM (bias mode): 1, the bias term once per block as bf16 products with the 32 groups
+// as k (K >= 1024); 2, once per block with the three pieces of X side by side in k (K
+// <= 512: 3 x 8 groups fit one MFMA); 0, per stage as an fp32 product over the stage's
+// four groups.
+template <bool SWIGLU, int GS, int BM>
 __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& lds) {
+  constexpr bool BB = BM != 0;
   constexpr int D = 2;  // weight register sets: the next stage's in flight
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,8 +322,9 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   };
   clear_sb();
   auto capture_sb = [&](int st, const StageW& w) __attribute__((always_inline)) {
-    const bool lo_half = (st >> 1) == q && (st & 1) == 0;  // groups 8q .. 8q+3
-    const bool hi_half = (st >> 1) == q && (st & 1) == 1;  // groups 8q+4 .. 8q+7
+    // BM 1: groups 8q .. 8q+3 and 8q+4 .. 8q+7; BM 2: groups 0 .. 3 and 4 .. 7 on every lane
+    const bool lo_half = BM == 2 ? st == 0 : (st >> 1) == q && (st & 1) == 0;
+    const bool hi_half = BM == 2 ? st == 1 : (st >> 1) == q && (st & 1) == 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       cs[j][0] = lo_half ? w.s[j][0] : cs[j][0];
@@ -345,6 +349,31 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, cbq[j], acc[f][j], 0, 0, 0);
+      }
+    }
+  };
+  // BM 2: k = 8 p + g takes piece p (0..2) of X and group g (0..7); b and s repeat
+  // over p; quarter q = 3 gives zeros.  b X and s X are then one MFMA each.
+  auto bias_block_packed = [&]() __attribute__((always_inline)) {
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+    u32x4_t bq[2], sq[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bq[j] = q < 3 ? cb[j] : z4;
+      sq[j] = q < 3 ? cs[j] : z4;
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f < nfv) {
+        u32x4_t xa = *(const u32x4_t*)(xp + (q < 3 ? q : 0) * XP_PIECE + (16 * f + m) * (2 * XG));
+        if (q == 3) xa = z4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4_t sx = mfma16x16x32(xa, sq[j], zero);
+          acc[f][j] = mfma16x16x32(xa, bq[j], acc[f][j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+        }
       }
     }
   };
@@ -427,7 +456,8 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
     lds_barrier();
     if (!BB) bias_term(st, cbq);
     if (st == NK - 1) {  // with BB: X of every group is in LDS since the first block's end
-      if (BB) bias_block();
+      if (BM == 1) bias_block();
+      if (BM == 2) bias_block_packed();
       epilogue(blk);
       reset();
       if (BB) clear_sb();
@@ -443,7 +473,7 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 
 // GS: scale group of MFMA steps 0 and 1 after the word swaps, read off the swapped
 // word numbers on entry (both orders compiled).
-template <bool SWIGLU, bool BB>
+template <bool SWIGLU, int BM>
 __global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char a0[A_BUF];
   __shared__ __attribute__((aligned(16))) unsigned char a1[A_BUF];
@@ -454,8 +484,8 @@ __global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
   const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
                                                   false, false);
   const int gs = __builtin_amdgcn_readfirstlane((int)(r[0] >> 3));
-  if (gs) wide_body<SWIGLU, 1, BB>(p, lds);
-  else wide_body<SWIGLU, 0, BB>(p, lds);
+  if (gs) wide_body<SWIGLU, 1, BM>(p, lds);
+  else wide_body<SWIGLU, 0, BM>(p, lds);
 }
 
 template <bool SWIGLU>
@@ -475,11 +505,12 @@ void launch_w(TiledParams p, int64_t n_tiles_bound, hipStream_t s) {
   const bool split = !(env && env[0] == '0');
   p.xcd_cus = split && xc >= 1 && per_b >= xc ? xc : 0;
   const int64_t per_xcd = p.xcd_cus ? per_b + (int64_t)(xc - 1) * (NUT - 1) : per_b;
-  // the bias once per block pays where a block has at least four stages (16 groups)
-  if (p.K >= 4 * WKS)
-    hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, true>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, false>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, p);
+  // the bias once per block: with the 32 groups as k from four stages (16 groups) up,
+  // with the pieces of X side by side in k up to two stages (8 groups)
+  const dim3 grid((unsigned)(8 * per_xcd)), block(512);
+  if (p.K >= 4 * WKS) hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, 1>), grid, block, 0, s, p);
+  else if (p.K <= 2 * WKS) hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, 2>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((q4_wide_kernel<SWIGLU, 0>), grid, block, 0, s, p);
 }
 
 }  // namespace

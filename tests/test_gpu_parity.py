@@ -147,13 +147,16 @@ def test_grouped_gemm_exact_integer(torch_cuda, case, bias_val, engine):
 @pytest.mark.parametrize("free_bias", [False, True])
 @pytest.mark.parametrize("epilogue", [0, 1])
 @pytest.mark.parametrize("counts", [[0, 3, 16, 29, 64, 90, 1], [250, 0, 131, 7, 384]])
-def test_grouped_gemm_float_vs_oracle(torch_cuda, epilogue, counts, free_bias, engine):
+@pytest.mark.parametrize("K", [1024, 768, 512])
+def test_grouped_gemm_float_vs_oracle(torch_cuda, K, epilogue, counts, free_bias, engine):
     """Float weights: the generator's (bias = -scale * (7.5 + 0.5 z) per group) and, with
-    free_bias, biases drawn independently of the scale and of either sign."""
+    free_bias, biases drawn independently of the scale and of either sign.  K = 1024, 768
+    and 512 take the three ways the wide-tile engine forms the bias term (once per block
+    over 32 groups, per stage, once per block with the pieces of X side by side)."""
     torch = torch_cuda
     rng = np.random.default_rng(7 + epilogue)
-    say(f"float gemm [{engine}] epilogue={epilogue} counts={counts} free_bias={free_bias}")
-    G, N, K = len(counts), 256, 1024
+    say(f"float gemm [{engine}] K={K} epilogue={epilogue} counts={counts} free_bias={free_bias}")
+    G, N = len(counts), 256
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(off[-1])
     cfg = wl.MoEConfig("g", 0, K, G - 1, 1, N // 2)
