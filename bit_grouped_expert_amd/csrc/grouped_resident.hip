@@ -13,10 +13,12 @@
 //   sum_c x[m,c] (s q[n,c] + b) = s * P' + (b - 128 s) * X,
 //   P' = sum_c x[m,c] (128 + q[n,c]),   X = sum_c x[m,c].
 // 128 + q is exactly the bf16 with bits 0x4300 | q (one AND-OR per pair of codes),
-// so P' is a bf16 matrix-core product with exact products.  X comes from the same
-// matrix cores, as the product of the activation fragment with a fragment of ones,
-// which leaves it in the accumulator layout of P'.  Each group then costs two FMAs
-// per output, whatever the bias.
+// so P' is a bf16 matrix-core product with exact products, and s * P' one FMA per
+// output and group.  X comes from the same matrix cores (the activation fragment times
+// a fragment of ones) and is kept in LDS as three bf16 pieces whose sum is X exactly;
+// at the end of each chunk the bias term is b X - 128 (s X), bf16 matrix-core products
+// of those pieces with the s and b words the chunk's stages streamed (exact products),
+// so it costs the same whatever the bias.
 //
 // Work decomposition.  Tiles hold up to 32 rows of one group.  A tile's weight
 // rows are cut into chunks of 128 or 256 rows; the list of (tile, chunk) pairs is
@@ -58,9 +60,11 @@ constexpr int SEG_CAP = 48;        // most tiles one workgroup may touch (host-c
 constexpr int PART_BYTES = 16384;  // partial sums / output staging
 
 __host__ __device__ constexpr int part_off(int K) { return 2 * (K / 8) * 256; }
-// row sums X of the tile's activations per 64-wide group, fp32 [K / 64][32 rows]
+// row sums X of the tile's activations per 64-wide group as three bf16 pieces whose sum
+// is X exactly: [piece 3][32 rows][32 groups]
+constexpr int XP_PIECE = 32 * 32 * 2;
 __host__ __device__ constexpr int xs_off(int K) { return part_off(K) + PART_BYTES; }
-__host__ __device__ constexpr int seg_off(int K) { return xs_off(K) + (K / 64) * 32 * 4; }
+__host__ __device__ constexpr int seg_off(int K) { return xs_off(K) + 3 * XP_PIECE; }
 __host__ __device__ constexpr int idx_off(int K) { return seg_off(K) + SEG_CAP * 16; }
 __host__ __device__ constexpr int lds_bytes(int K) { return idx_off(K) + SEG_CAP * 32 * 4; }
 static_assert(lds_bytes(kResidentMaxK) <= 160 * 1024, "LDS budget");
@@ -203,19 +207,10 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   // runs in three phases kept apart by scheduling barriers, so that matrix results are
   // consumed only after all of the half's chains are issued: operands (LDS reads and
   // unpacked weights), then the MFMA chains, then acc += s * P'.  The bias term
-  // (b - 128 s) X is not applied here: lane quarter q keeps (b - 128 s) of group q of
-  // the stage for the fp32 matrix-core product at the end of the chunk.
-  auto compute = [&](const StageW& w, int st, float* cbq, auto nf_tag) __attribute__((always_inline)) {
+  // (b - 128 s) X is not applied here: the stage's s and b words are kept for the bias
+  // product at the end of the chunk.
+  auto compute = [&](const StageW& w, int st, auto nf_tag) __attribute__((always_inline)) {
     constexpr int NF = decltype(nf_tag)::value;
-    // (b - 128 s) of group q of this stage (q = lane quarter), both weight fragments
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t sw = (q & 2) ? w.s[j][1] : w.s[j][0];
-      const uint32_t bw = (q & 2) ? w.b[j][1] : w.b[j][0];
-      const float sq = (q & 1) ? bf16hi_to_f32(sw) : bf16lo_to_f32(sw);
-      const float bq = (q & 1) ? bf16hi_to_f32(bw) : bf16lo_to_f32(bw);
-      cbq[j] = fmaf(-128.f, sq, bq);
-    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const unsigned char* ab = smem + ((uint32_t)st * 2 + hh) * 4096u;
@@ -275,43 +270,91 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   // compiler's wait counts stay exact across the loop.
   StageW W[D];
 
+  // The s and b words this lane feeds to the bias product, [weight fragment] x eight
+  // groups of this wavefront's 4 NST: with NST <= 2 groups 0 .. 7 on every lane, with
+  // NST >= 3 groups 8 (q & 1) .. 8 (q & 1) + 7.  Slots of groups past 4 NST stay zero.
+  u32x4_t sw_s[2], sw_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sw_s[j] = u32x4_t{0u, 0u, 0u, 0u};
+    sw_b[j] = sw_s[j];
+  }
+  auto capture_sb = [&](int d, const StageW& w) __attribute__((always_inline)) {
+    const int h = d & 1;  // groups 4 d .. 4 d + 3 of the wavefront: words 2 h, 2 h + 1
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (NST <= 2 || d < 2) {
+        const bool take = NST <= 2 || (q & 1) == 0;
+        sw_s[j][2 * h] = take ? w.s[j][0] : sw_s[j][2 * h];
+        sw_s[j][2 * h + 1] = take ? w.s[j][1] : sw_s[j][2 * h + 1];
+        sw_b[j][2 * h] = take ? w.b[j][0] : sw_b[j][2 * h];
+        sw_b[j][2 * h + 1] = take ? w.b[j][1] : sw_b[j][2 * h + 1];
+      } else {
+        const bool take = (q & 1) == 1;
+        sw_s[j][2 * h] = take ? w.s[j][0] : sw_s[j][2 * h];
+        sw_s[j][2 * h + 1] = take ? w.s[j][1] : sw_s[j][2 * h + 1];
+        sw_b[j][2 * h] = take ? w.b[j][0] : sw_b[j][2 * h];
+        sw_b[j][2 * h + 1] = take ? w.b[j][1] : sw_b[j][2 * h + 1];
+      }
+    }
+  };
   // One chunk: NST stages, stage s on register set s (D == NST, so the rotation starts
   // over with every chunk).  The loads stay outside the branch on the fragment count:
   // identical loads in both arms would be merged into the join block, after the matrix
-  // work, which would turn the prefetch into load-then-wait.  cbk[s][j]: the lane's
-  // (b - 128 s) of stage s, kept for the bias product.
-  float cbk[NST][2];
+  // work, which would turn the prefetch into load-then-wait.
   auto run_chunk = [&](int nfv) __attribute__((always_inline)) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       pf_load(W[(d + D - 1) % D]);
-      if (nfv == 2) compute(W[d], kbase + d, cbk[d], std::integral_constant<int, 2>{});
-      else compute(W[d], kbase + d, cbk[d], std::integral_constant<int, 1>{});
+      if (nfv == 2) compute(W[d], kbase + d, std::integral_constant<int, 2>{});
+      else compute(W[d], kbase + d, std::integral_constant<int, 1>{});
+      capture_sb(d, W[d]);
     }
   };
-  // acc += sum over this wavefront's groups of (b - 128 s) X, on the fp32 matrix cores
-  // (v_mfma_f32_16x16x4_f32: lane l gives A[row l % 16][k = l / 16] and
-  // B[k = l / 16][column l % 16]): step s takes the four groups of stage s, k = group.
-  const float* xs = (const float*)(smem + xs_off(K));
+  // acc += sum over this wavefront's groups of (b - 128 s) X, exactly up to fp32
+  // rounding, as bf16 matrix-core products (v_mfma_f32_16x16x32_bf16: lane (m, q) gives
+  // k = 8 q .. 8 q + 7 of row m, lane (n, q) the same k of column n): b X and s X over
+  // the three pieces of X, then acc += b X - 128 (s X).  NST <= 2: k = 8 p + g, piece p
+  // of X (quarter 3 zero), groups g 0 .. 7.  NST >= 3: first product quarters (piece,
+  // group half) = (hi, 0), (hi, 1), (mid, 0), (mid, 1), second (lo, 0), (lo, 1), zero.
+  const unsigned char* xpb = smem + xs_off(K) + 8 * kbase;  // group 4 kbase, 2 bytes each
   auto bias_term = [&](int nfv) __attribute__((always_inline)) {
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int d = 0; d < NST; ++d) {
-      const int g = 4 * (kbase + d) + q;
+    for (int f = 0; f < 2; ++f)
+      if (f < nfv) {
+        const unsigned char* xr = xpb + (16 * f + m) * 64;
+        if constexpr (NST <= 2) {
+          u32x4_t xa = *(const u32x4_t*)(xr + (q < 3 ? q : 0) * XP_PIECE);
+          if (q == 3) xa = z4;
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        if (f < nfv) {
-          const float xa = xs[g * 32 + 16 * f + m];
+          for (int j = 0; j < 2; ++j) {
+            const u32x4_t bq = q < 3 ? sw_b[j] : z4, sq = q < 3 ? sw_s[j] : z4;
+            const f32x4_t sx = mfma16x16x32(xa, sq, zero);
+            acc[f][j] = mfma16x16x32(xa, bq, acc[f][j]);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, cbk[d][j], acc[f][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+          }
+        } else {
+          const u32x4_t x1 = *(const u32x4_t*)(xr + (q >> 1) * XP_PIECE + 16 * (q & 1));
+          u32x4_t x2 = *(const u32x4_t*)(xr + 2 * XP_PIECE + 16 * (q & 1));
+          if (q >= 2) x2 = z4;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x4_t sx = mfma16x16x32(x2, sw_s[j], mfma16x16x32(x1, sw_s[j], zero));
+            acc[f][j] = mfma16x16x32(x2, sw_b[j], mfma16x16x32(x1, sw_b[j], acc[f][j]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+          }
         }
-    }
+      }
   };
 
-  // X[group][row] of the tile: the product of each group's two 32-K activation fragments
-  // with a fragment of ones, written by the lanes of column 0; then a barrier
+  // X of the tile: the product of each group's two 32-K activation fragments with a
+  // fragment of ones, written by the lanes of column 0 as three bf16 pieces (each the top
+  // eight significant bits of what the previous ones left); then a barrier
   auto tile_row_sums = [&](int nfv) __attribute__((always_inline)) {
-    float* xw = (float*)(smem + xs_off(K));
+    unsigned char* xw = smem + xs_off(K);
     const int KG4 = K >> 6;
     for (int pi = wave; pi < nfv * KG4; pi += 8) {
       const int f = pi / KG4, g = pi - f * KG4;
@@ -319,7 +362,19 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       const u32x4_t a0 = *(const u32x4_t*)ab;
       const u32x4_t a1 = *(const u32x4_t*)(ab + 256);
       const f32x4_t X = mfma16x16x32(a1, ones, mfma16x16x32(a0, ones, zero));
-      if (m == 0) *(f32x4_t*)(xw + g * 32 + 16 * f + 4 * q) = X;
+      if (m == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t hi = __float_as_uint(X[i]) & 0xFFFF0000u;
+          const float r1 = X[i] - __uint_as_float(hi);
+          const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+          const uint32_t lo = __float_as_uint(r1 - __uint_as_float(mid)) & 0xFFFF0000u;
+          const int off = (16 * f + 4 * q + i) * 64 + 2 * g;
+          *(uint16_t*)(xw + off) = (uint16_t)(hi >> 16);
+          *(uint16_t*)(xw + XP_PIECE + off) = (uint16_t)(mid >> 16);
+          *(uint16_t*)(xw + 2 * XP_PIECE + off) = (uint16_t)(lo >> 16);
+        }
+      }
     }
     lds_barrier();
   };
@@ -353,6 +408,9 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
         const int cb = wave + 8 * i;
         if (f < nf0 && cb < per_f) *(u32x4_t*)(smem + f * A_FRAG + cb * 1024 + 16 * l) = a_first[f][i];
       }
+    // the pieces of X zeroed once (groups past K stay zero)
+    for (int o = 16 * tid; o < 3 * XP_PIECE; o += 16 * 512)
+      *(u32x4_t*)(smem + xs_off(K) + o) = u32x4_t{0u, 0u, 0u, 0u};
     lds_barrier();
     tile_row_sums(nf0);
     cur_seg = t.w;
