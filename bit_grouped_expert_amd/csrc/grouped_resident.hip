@@ -16,9 +16,12 @@
 // so P' is a bf16 matrix-core product with exact products, and s * P' one FMA per
 // output and group.  X comes from the same matrix cores (the activation fragment times
 // a fragment of ones) and is kept in LDS as three bf16 pieces whose sum is X exactly;
-// at the end of each chunk the bias term is b X - 128 (s X), bf16 matrix-core products
-// of those pieces with the s and b words the chunk's stages streamed (exact products),
-// so it costs the same whatever the bias.
+// once per chunk the bias term is b X - 128 (s X), bf16 matrix-core products of those
+// pieces with the chunk's s and b words (exact products), so it costs the same
+// whatever the bias: with four stages per chunk it is the accumulators' starting value,
+// formed while the chunk's first weight stage is in flight (the s and b words loaded
+// with the chunk's prefetch setup); with fewer it is added at the chunk's end from the
+// words the stages streamed.
 //
 // Work decomposition.  Tiles hold up to 32 rows of one group.  A tile's weight
 // rows are cut into chunks of 128 or 256 rows; the list of (tile, chunk) pairs is
@@ -141,6 +144,14 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   const uint16_t* pf_sc = nullptr;
   const uint16_t* pf_bi = nullptr;
   uint32_t pf_co[2], pf_so[2];
+  // The s and b words of the prefetched chunk that this lane feeds to the chunk's bias
+  // product: eight groups of this wavefront's 4 NST, from group sb_g0 (NST <= 2: groups
+  // 0 .. 7; NST >= 3: groups 8 (q & 1) .. + 7), as two 8-byte halves; the second half
+  // only where its groups exist (else it is loaded again from the first and not used).
+  constexpr bool kStartBias = NST >= 3;  // else the product at the chunk's end
+  const int sb_g0 = NST >= 3 ? 8 * (q & 1) : 0;
+  const bool sb_hi = sb_g0 + 4 < 4 * NST;
+  u32x2_t sb_s[2][2], sb_b[2][2];  // [weight fragment][half]
   auto pf_chunk = [&]() __attribute__((always_inline)) {
     const int4 t = seg_of(pf_ch);
     const int cin = pf_ch - (pf_ch / NCH) * NCH;
@@ -163,6 +174,15 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     pf_co[1] = ((uint32_t)n1 * KW + 4 * q) * 4u;
     pf_so[0] = (uint32_t)n0 * KG * 2u;
     pf_so[1] = (uint32_t)n1 * KG * 2u;
+#pragma unroll
+    for (int j = 0; j < 2 && kStartBias; ++j) {
+      const uint32_t o = pf_so[j] + (uint32_t)(4 * kbase + sb_g0) * 2u;
+      const uint32_t o2 = sb_hi ? o + 8u : o;
+      sb_s[j][0] = ld<u32x2_t>(pf_sc, o);
+      sb_s[j][1] = ld<u32x2_t>(pf_sc, o2);
+      sb_b[j][0] = ld<u32x2_t>(pf_bi, o);
+      sb_b[j][1] = ld<u32x2_t>(pf_bi, o2);
+    }
   };
   auto pf_load = [&](StageW& w) __attribute__((always_inline)) {
     const int st = kbase + pf_s;
@@ -207,8 +227,8 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   // runs in three phases kept apart by scheduling barriers, so that matrix results are
   // consumed only after all of the half's chains are issued: operands (LDS reads and
   // unpacked weights), then the MFMA chains, then acc += s * P'.  The bias term
-  // (b - 128 s) X is not applied here: the stage's s and b words are kept for the bias
-  // product at the end of the chunk.
+  // (b - 128 s) X is the accumulators' starting value (bias_init, NST >= 3) or added at
+  // the chunk's end (bias_term, NST <= 2).
   auto compute = [&](const StageW& w, int st, auto nf_tag) __attribute__((always_inline)) {
     constexpr int NF = decltype(nf_tag)::value;
 #pragma unroll
@@ -280,6 +300,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     sw_b[j] = sw_s[j];
   }
   auto capture_sb = [&](int d, const StageW& w) __attribute__((always_inline)) {
+    if constexpr (kStartBias) return;
     const int h = d & 1;  // groups 4 d .. 4 d + 3 of the wavefront: words 2 h, 2 h + 1
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -311,13 +332,62 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       capture_sb(d, W[d]);
     }
   };
+  // acc starts as the chunk's bias term, sum over this wavefront's groups of
+  // (b - 128 s) X, exactly up to fp32 rounding, formed while the chunk's first weight
+  // stage is still in flight: bf16 matrix-core products (v_mfma_f32_16x16x32_bf16: lane
+  // (m, q) gives k = 8 q .. 8 q + 7 of row m, lane (n, q) the same k of column n) of b
+  // and s with the three pieces of X, then acc = b X - 128 (s X).  NST <= 2: k = 8 p + g,
+  // piece p of X (quarter 3 zero), groups g 0 .. 7.  NST >= 3: first product quarters
+  // (piece, group half) = (hi, 0), (hi, 1), (mid, 0), (mid, 1), second (lo, 0), (lo, 1),
+  // zero.  Group slots past 4 NST have zero s and b.
+  const unsigned char* xpb = smem + xs_off(K) + 8 * kbase;  // group 4 kbase, 2 bytes each
+  auto bias_init = [&](int nfv) __attribute__((always_inline)) {
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+    u32x4_t bw[2], sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bw[j] = u32x4_t{sb_b[j][0][0], sb_b[j][0][1], sb_hi ? sb_b[j][1][0] : 0u, sb_hi ? sb_b[j][1][1] : 0u};
+      sw[j] = u32x4_t{sb_s[j][0][0], sb_s[j][0][1], sb_hi ? sb_s[j][1][0] : 0u, sb_hi ? sb_s[j][1][1] : 0u};
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      if (f < nfv) {
+        const unsigned char* xr = xpb + (16 * f + m) * 64;
+        if constexpr (NST <= 2) {
+          u32x4_t xa = *(const u32x4_t*)(xr + (q < 3 ? q : 0) * XP_PIECE);
+          if (q == 3) xa = z4;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x4_t sx = mfma16x16x32(xa, sw[j], zero);
+            acc[f][j] = mfma16x16x32(xa, bw[j], zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+          }
+        } else {
+          const u32x4_t x1 = *(const u32x4_t*)(xr + (q >> 1) * XP_PIECE + 16 * (q & 1));
+          u32x4_t x2 = *(const u32x4_t*)(xr + 2 * XP_PIECE + 16 * (q & 1));
+          if (q >= 2) x2 = z4;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x4_t sx = mfma16x16x32(x2, sw[j], mfma16x16x32(x1, sw[j], zero));
+            acc[f][j] = mfma16x16x32(x2, bw[j], mfma16x16x32(x1, bw[j], zero));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][j][i] = fmaf(-128.f, sx[i], acc[f][j][i]);
+          }
+        }
+      } else {
+        acc[f][0] = zero;
+        acc[f][1] = zero;
+      }
+    }
+  };
+
   // acc += sum over this wavefront's groups of (b - 128 s) X, exactly up to fp32
   // rounding, as bf16 matrix-core products (v_mfma_f32_16x16x32_bf16: lane (m, q) gives
   // k = 8 q .. 8 q + 7 of row m, lane (n, q) the same k of column n): b X and s X over
   // the three pieces of X, then acc += b X - 128 (s X).  NST <= 2: k = 8 p + g, piece p
   // of X (quarter 3 zero), groups g 0 .. 7.  NST >= 3: first product quarters (piece,
   // group half) = (hi, 0), (hi, 1), (mid, 0), (mid, 1), second (lo, 0), (lo, 1), zero.
-  const unsigned char* xpb = smem + xs_off(K) + 8 * kbase;  // group 4 kbase, 2 bytes each
   auto bias_term = [&](int nfv) __attribute__((always_inline)) {
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -439,12 +509,17 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       tile_row_sums(nfv);
       cur_seg = k;
     }
+    if constexpr (kStartBias) {
+      bias_init(nfv);
+      run_chunk(nfv);
+    } else {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[f][j] = zero;
-    run_chunk(nfv);
-    bias_term(nfv);
+        for (int j = 0; j < 2; ++j) acc[f][j] = zero;
+      run_chunk(nfv);
+      bias_term(nfv);
+    }
 
     // ---- end of chunk: halves of K meet through LDS, then bf16 rows go out
     bool owner = true;
