@@ -160,8 +160,10 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
  *   W          q [n_groups, N, K/8], scale/bias [n_groups, N, K/64]
  *   ws         >= moe_grouped_gemm_q4_workspace_bytes(n_groups, rows_total, a_rows, K).
  * Arithmetic: no weight is rounded; each 64-wide group's partial sum is formed on
- * the matrix cores from the exact values 128 + q and scaled in fp32, so H is the
- * fp32-accumulated product with the exactly dequantized weights.  The environment
+ * the matrix cores from the exact values 128 + q and scaled in fp32, and the bias
+ * part (b - 128 s) X (X: the row's sum over the group) comes from exact products of
+ * b, s and X (X split into three bf16 pieces that sum to it exactly, or X itself in
+ * fp32), so H is the fp32-accumulated product with the exactly dequantized weights.  The environment
  * variable MOEQ4_GEMM=rows selects an older engine with the same arithmetic (kept
  * for comparison). */
 moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
