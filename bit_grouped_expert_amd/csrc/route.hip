@@ -327,16 +327,17 @@ __global__ __launch_bounds__(512) void router_logits_wide_kernel(
   }
 }
 
-// Fewer tokens (D % 256 == 0): the fp32 matrix cores on R itself (v_mfma_f32_16x16x4_f32,
-// bf16 x widened exactly), so no split of R is needed.  Workgroup tile: 16 tokens x 32
-// experts; its sixteen wavefronts (four per SIMD, to hide the LDS and load latencies) are
-// two 16-expert tiles times eight 32-K parts of each 256-K chunk, with two accumulators
-// each, added through LDS at the end in a fixed order.  The chunk's R
-// rows (1 KB each) and x rows go through padded LDS rows with line-whole loads, one
-// chunk ahead in VGPRs.  In MFMA step s of a 16-K group, lane (m, q) supplies
-// k = 16 g + 4 q + s of token row m and of expert column m, so its operands of four
-// steps are one 16-byte read of R and one 8-byte read of x.  The workgroups of the
-// first expert column also write the prepared copy of x from the x pieces they load.
+// Fewer tokens (D % 256 == 0): R itself, fp32, split in registers into three bf16 pieces
+// that sum to it exactly, on the bf16 matrix cores (x is bf16 already, so every product
+// is exact; an earlier form on the fp32 matrix cores, v_mfma_f32_16x16x4_f32, took 11.7
+// against 10.3 us at 512 tokens).  Workgroup tile: 16 tokens x 32 experts; its sixteen
+// wavefronts (four per SIMD, to hide the LDS and load latencies) are two 16-expert tiles
+// times eight 32-K parts of each 256-K chunk, with two accumulators each, added through
+// LDS at the end in a fixed order.  The chunk's R rows (1 KB each) and x rows go through
+// padded LDS rows with line-whole loads, one chunk ahead in VGPRs.  A wavefront's 32 k
+// of a chunk are one 16x16x32 step: lane (m, q) reads x of token m and R of expert m at
+// k = 8 q .. 8 q + 7.  The workgroups of the first expert column also write the
+// prepared copy of x from the x pieces they load.
 constexpr int kF32KC = 256;
 constexpr int kF32RRow = kF32KC * 4 + 16;  // padded LDS row of R, bytes
 constexpr int kF32XRow = kF32KC * 2 + 16;  // padded LDS row of x, bytes
@@ -385,18 +386,34 @@ __global__ __launch_bounds__(kF32Threads) void router_logits_f32_kernel(
     if (prep && xv) *(u32x4_t*)(xprep + (int64_t)(t0 + xr) * D + ch * kF32KC + 8 * xc) = interleave8(pc.x);
   };
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  // The wavefront's 32 k of the chunk as one bf16 step (v_mfma_f32_16x16x32_bf16: lane
+  // (m, q) gives x of token m and R of expert m at k = 8 q .. 8 q + 7): R split into
+  // three bf16 pieces by truncation (hi, mid, lo: each the top eight significant bits of
+  // what the previous ones left, so they sum to R exactly) and every product x R_piece
+  // exact, accumulated in fp32.
   auto compute = [&](int buf) __attribute__((always_inline)) {
-    const unsigned char* rb = &rs[buf][(16 * tile + m) * kF32RRow + kq * 128];
-    const unsigned char* xb = &xsh[buf][m * kF32XRow + kq * 64];
+    const unsigned char* rb = &rs[buf][(16 * tile + m) * kF32RRow + kq * 128 + 32 * q];
+    const u32x4_t xa = *(const u32x4_t*)&xsh[buf][m * kF32XRow + kq * 64 + 16 * q];
+    const f32x4_t r0 = *(const f32x4_t*)rb, r1 = *(const f32x4_t*)(rb + 16);
+    const float r[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    uint32_t ph[8], pm[8], pl[8];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const f32x4_t rv = *(const f32x4_t*)(rb + (16 * g + 4 * q) * 4);
-      const u32x2_t xw = *(const u32x2_t*)(xb + (16 * g + 4 * q) * 2);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo_to_f32(xw[0]), rv[0], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi_to_f32(xw[0]), rv[1], acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo_to_f32(xw[1]), rv[2], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi_to_f32(xw[1]), rv[3], acc1, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      ph[i] = __float_as_uint(r[i]) & 0xFFFF0000u;
+      const float e1 = r[i] - __uint_as_float(ph[i]);
+      pm[i] = __float_as_uint(e1) & 0xFFFF0000u;
+      pl[i] = __float_as_uint(e1 - __uint_as_float(pm[i])) & 0xFFFF0000u;
     }
+    u32x4_t bh, bm, bl;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      bh[w] = (ph[2 * w] >> 16) | ph[2 * w + 1];
+      bm[w] = (pm[2 * w] >> 16) | pm[2 * w + 1];
+      bl[w] = (pl[2 * w] >> 16) | pl[2 * w + 1];
+    }
+    acc0 = mfma16x16x32(xa, bh, acc0);
+    acc1 = mfma16x16x32(xa, bm, acc1);
+    acc0 = mfma16x16x32(xa, bl, acc0);
   };
   // chunk ch in buffer ch & 1; the other buffer was last read in the previous chunk,
   // before the last barrier
