@@ -88,6 +88,7 @@ GEMM_INT_CASES = [
     ([127, 128, 129, 0, 300, 1], 384, 384, True),   # K % 128 == 0: streamed, 64-row tiles
     ([5, 0, 70, 3], 320, 128, True),                # one 128-K stage per item
     ([0, 1, 17, 33, 100], 256, 1024, True),         # two halves of K, two 256-K stages each
+    ([40, 0, 129, 300], 256, 256, True),            # one 256-K stage: four groups in every bias form
     ([5, 0, 70, 3, 16], 512, 1536, False),          # halves of three stages, no prefetch
     ([1, 31, 32, 33], 768, 256, False),             # one stage over the whole K
     ([40, 2, 0, 27], 256, 512, True),               # whole K per wavefront, two stages
