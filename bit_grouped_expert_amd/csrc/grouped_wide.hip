@@ -12,7 +12,9 @@
 // term sum_g (b - 128 s) X.  Where K >= 1024 the bias term is formed once per block of
 // weight rows, as bf16 matrix-core products with all 32 groups as k: b X and s X with
 // X split exactly into three bf16 pieces (b and s are bf16 already, so every product is
-// exact), then acc += b X - 128 (s X).  Where K <= 512 (the down GEMM) the three pieces
+// exact), then acc += b X - 128 (s X).  The lane's s and b words of the block are loaded
+// at its first stage, and the product follows that stage once X is complete (every block
+// after a workgroup's first), so that it does not delay the block's end.  Where K <= 512 (the down GEMM) the three pieces
 // of X sit side by side in the 32-wide k (3 x 8 groups), so b X and s X are one MFMA
 // each.  In between (K = 768) the bias stays a per-stage fp32 product
 // (v_mfma_f32_16x16x4_f32, the stage's four groups as k); timing the engine without any
@@ -312,7 +314,35 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   // lane (m, q) gives X of row m and groups 8q .. 8q+7, lane (n, q) b or s of column n and
   // the same groups), over the three pieces of X; then acc += b X - 128 (s X).  sb: this
   // lane's s and b words of groups 8q .. 8q+7, captured from the stages as they passed.
-  u32x4_t cs[2], cb[2];  // [weight fragment]: s, b of groups 8q .. 8q+7 (zero past K)
+  // BM 1: the s and b words of the block that this lane feeds to the bias product
+  // (groups 8q .. 8q+7), loaded at the block's first stage as two 8-byte halves; a half
+  // past K is loaded again from the row's first groups and not used.  BM 2: groups 0 .. 7
+  // on every lane, taken from the stages' words as they stream (capture_sb).
+  const int sb_g0 = 8 * q;
+  const bool sb_lo = sb_g0 + 4 <= KG, sb_hi = sb_g0 + 8 <= KG;
+  u32x2_t sbs[2][2], sbb[2][2];  // [weight fragment][half]
+  auto load_sb = [&](int blk) __attribute__((always_inline)) {
+    int n0, n1;
+    if (SWIGLU) {
+      const int u = 8 * blk + wave;
+      n0 = 16 * u + m;
+      n1 = (N >> 1) + 16 * u + m;
+    } else {
+      n0 = 256 * blk + 32 * wave + m;
+      n1 = n0 + 16;
+    }
+    const uint32_t so[2] = {(uint32_t)n0 * KG * 2u, (uint32_t)n1 * KG * 2u};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t o0 = sb_lo ? so[j] + 2u * sb_g0 : so[j];
+      const uint32_t o1 = sb_hi ? so[j] + 2u * sb_g0 + 8u : so[j];
+      sbs[j][0] = ld<u32x2_t>(Ws, o0);
+      sbs[j][1] = ld<u32x2_t>(Ws, o1);
+      sbb[j][0] = ld<u32x2_t>(Wb, o0);
+      sbb[j][1] = ld<u32x2_t>(Wb, o1);
+    }
+  };
+  u32x4_t cs[2], cb[2];  // the words as MFMA operands (zero past K)
   auto clear_sb = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -322,9 +352,7 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
   };
   clear_sb();
   auto capture_sb = [&](int st, const StageW& w) __attribute__((always_inline)) {
-    // BM 1: groups 8q .. 8q+3 and 8q+4 .. 8q+7; BM 2: groups 0 .. 3 and 4 .. 7 on every lane
-    const bool lo_half = BM == 2 ? st == 0 : (st >> 1) == q && (st & 1) == 0;
-    const bool hi_half = BM == 2 ? st == 1 : (st >> 1) == q && (st & 1) == 1;
+    const bool lo_half = st == 0, hi_half = st == 1;  // groups 0 .. 3, 4 .. 7
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       cs[j][0] = lo_half ? w.s[j][0] : cs[j][0];
@@ -335,6 +363,15 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
       cb[j][1] = lo_half ? w.b[j][1] : cb[j][1];
       cb[j][2] = hi_half ? w.b[j][0] : cb[j][2];
       cb[j][3] = hi_half ? w.b[j][1] : cb[j][3];
+    }
+  };
+  auto take_sb = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cs[j] = u32x4_t{sb_lo ? sbs[j][0][0] : 0u, sb_lo ? sbs[j][0][1] : 0u, sb_hi ? sbs[j][1][0] : 0u,
+                      sb_hi ? sbs[j][1][1] : 0u};
+      cb[j] = u32x4_t{sb_lo ? sbb[j][0][0] : 0u, sb_lo ? sbb[j][0][1] : 0u, sb_hi ? sbb[j][1][0] : 0u,
+                      sb_hi ? sbb[j][1][1] : 0u};
     }
   };
   // Per stage (without BB): acc += (b - 128 s) X over the stage's four groups
@@ -378,6 +415,7 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
     }
   };
   auto bias_block = [&]() __attribute__((always_inline)) {
+    take_sb();
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f < nfv) {
@@ -448,19 +486,23 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
     const int vn = v + 1 < UT ? v + 1 : v;  // the last stage loads itself again
     issue_a(vn - (vn / NK) * NK, next_a);
     pf_load(fresh);
+    if (BM == 1 && st == 0) load_sb(blk);
     float cbq[2];
     compute(cur, cur_a, cbq);
-    if (BB) capture_sb(st, cur);
+    if (BM == 2) capture_sb(st, cur);
+    // BM 1: after the workgroup's first block X is in LDS, and the block's bias product
+    // follows its first stage instead of delaying its end
+    if (BM == 1 && vb > 0 && st == 0) bias_block();
     if (vb == 0) row_sums(st, cur_a);  // X during the first block of this workgroup
     wait_vmcnt0();
     lds_barrier();
     if (!BB) bias_term(st, cbq);
-    if (st == NK - 1) {  // with BB: X of every group is in LDS since the first block's end
-      if (BM == 1) bias_block();
+    if (st == NK - 1) {  // X of every group is in LDS from the first block's end
+      if (BM == 1 && vb == 0) bias_block();
       if (BM == 2) bias_block_packed();
       epilogue(blk);
       reset();
-      if (BB) clear_sb();
+      if (BM == 2) clear_sb();
     }
   };
   int v = 0;
