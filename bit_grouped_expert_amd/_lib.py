@@ -37,6 +37,16 @@ class moe_q4_ffn(C.Structure):
     _fields_ = [("gate_up", moe_q4), ("down", moe_q4)]
 
 
+MOE_ENGINE_AUTO, MOE_ENGINE_GROUPED, MOE_ENGINE_RESIDENT, MOE_ENGINE_WIDE = range(4)
+ENGINES = {"auto": MOE_ENGINE_AUTO, "grouped": MOE_ENGINE_GROUPED,
+           "resident": MOE_ENGINE_RESIDENT, "wide": MOE_ENGINE_WIDE}
+N_STAGE_EVENTS = 6
+
+
+class moe_layer_opts(C.Structure):
+    _fields_ = [("engine", C.c_int32), ("reserved", C.c_int32), ("events", C.POINTER(C.c_void_p))]
+
+
 class moe_ws_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in
                 ("topk_idx", "topk_w", "offsets", "sorted_tok", "slot_row", "act", "y", "total")]
@@ -65,13 +75,20 @@ _SIGS = {
     "moe_layer_forward": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
                                     C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn), C.c_void_p,
                                     C.c_void_p, C.c_size_t, C.c_void_p]),
-    "moe_layer_forward_events": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
-                                           C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn), C.c_void_p,
-                                           C.c_void_p, C.c_size_t, C.POINTER(C.c_void_p),
-                                           C.c_void_p]),
+    "moe_layer_forward_ex": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
+                                       C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn), C.c_void_p,
+                                       C.c_void_p, C.c_size_t, C.POINTER(moe_layer_opts),
+                                       C.c_void_p]),
+    "moe_grouped_gemm_q4_ex": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                         C.c_int32, C.c_void_p, C.c_void_p, moe_q4, C.c_int32,
+                                         C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32,
+                                         C.c_void_p]),
+    "moe_chunked_workspace_bytes": (C.c_size_t, [C.POINTER(moe_shape), C.c_int32]),
+    "moe_layer_forward_chunked": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
+                                            C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn),
+                                            C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                            C.c_void_p]),
 }
-
-N_STAGE_EVENTS = 6
 
 
 def lib() -> C.CDLL:
@@ -160,12 +177,25 @@ def moe_permute(shp, topk_idx, offsets, sorted_tok, slot_row, ws, ws_bytes=None,
                              _p(slot_row), _p(ws), ws_bytes, _stream(stream)), "moe_permute")
 
 
+def _engine(engine) -> int:
+    return ENGINES[engine] if isinstance(engine, str) else int(engine)
+
+
 def moe_grouped_gemm_q4(n_groups, rows_total, N, K, A, a_rows, a_row_index, offsets, W: moe_q4,
                         epilogue, Cout, ws, ws_bytes=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib().moe_grouped_gemm_q4(n_groups, rows_total, N, K, _p(A), a_rows, _p(a_row_index),
                                      _p(offsets), W, epilogue, _p(Cout), _p(ws), ws_bytes,
                                      _stream(stream)), "moe_grouped_gemm_q4")
+
+
+def moe_grouped_gemm_q4_ex(n_groups, rows_total, N, K, A, a_rows, a_row_index, offsets, W: moe_q4,
+                           epilogue, Cout, ws, engine, ws_bytes=None, stream=None):
+    """engine: a MOE_ENGINE_* value or one of the names in ENGINES."""
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_grouped_gemm_q4_ex(n_groups, rows_total, N, K, _p(A), a_rows, _p(a_row_index),
+                                        _p(offsets), W, epilogue, _p(Cout), _p(ws), ws_bytes,
+                                        _engine(engine), _stream(stream)), "moe_grouped_gemm_q4_ex")
 
 
 def moe_combine(shp, y_sorted, slot_row, topk_w, shared_out, out, stream=None):
@@ -181,13 +211,36 @@ def moe_layer_forward(shp, x, router_w, experts: moe_q4_ffn, shared, out, ws, ws
                                    _p(out), _p(ws), ws_bytes, _stream(stream)), "moe_layer_forward")
 
 
-def moe_layer_forward_events(shp, x, router_w, experts: moe_q4_ffn, shared, out, ws, events,
-                             ws_bytes=None, stream=None):
-    """events: sequence of N_STAGE_EVENTS torch.cuda.Event (or raw hipEvent_t ints / None)."""
+def layer_opts(engine="auto", events=None) -> moe_layer_opts:
+    """events: None or a sequence of N_STAGE_EVENTS torch.cuda.Event / raw hipEvent_t ints / None.
+    The returned structure keeps the event array alive."""
+    o = moe_layer_opts(_engine(engine), 0, None)
+    if events is not None:
+        raw = (C.c_void_p * N_STAGE_EVENTS)(*[
+            None if e is None else (e if isinstance(e, int) else e.cuda_event) for e in events])
+        o._events_keep = raw
+        o.events = C.cast(raw, C.POINTER(C.c_void_p))
+    return o
+
+
+def moe_layer_forward_ex(shp, x, router_w, experts: moe_q4_ffn, shared, out, ws, opts=None,
+                         ws_bytes=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     sh = C.byref(shared) if shared is not None else None
-    raw = (C.c_void_p * N_STAGE_EVENTS)(*[
-        None if e is None else (e if isinstance(e, int) else e.cuda_event) for e in events])
-    _check(lib().moe_layer_forward_events(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
-                                          _p(out), _p(ws), ws_bytes, raw, _stream(stream)),
-           "moe_layer_forward_events")
+    op = C.byref(opts) if opts is not None else None
+    _check(lib().moe_layer_forward_ex(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
+                                      _p(out), _p(ws), ws_bytes, op, _stream(stream)),
+           "moe_layer_forward_ex")
+
+
+def moe_chunked_workspace_bytes(shp: moe_shape, chunk_tokens: int) -> int:
+    return lib().moe_chunked_workspace_bytes(C.byref(shp), chunk_tokens)
+
+
+def moe_layer_forward_chunked(shp, x, router_w, experts: moe_q4_ffn, shared, out, chunk_tokens, ws,
+                              ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    sh = C.byref(shared) if shared is not None else None
+    _check(lib().moe_layer_forward_chunked(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
+                                           _p(out), chunk_tokens, _p(ws), ws_bytes,
+                                           _stream(stream)), "moe_layer_forward_chunked")

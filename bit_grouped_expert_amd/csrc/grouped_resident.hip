@@ -601,7 +601,8 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 // orders are compiled, so the result never depends on the swap's direction.
 template <bool SWIGLU, int NST>
 __global__ __launch_bounds__(512, 1) void q4_resident_kernel(ResidentParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_dyn[];
+  // sized for the largest K: every launch fits without a per-kernel attribute
+  __shared__ __attribute__((aligned(16))) unsigned char smem_dyn[lds_bytes(kResidentMaxK)];
   const int l = threadIdx.x & 63;
   const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
                                                   false, false);
@@ -614,14 +615,7 @@ namespace {
 
 template <bool SWIGLU, int NST>
 void launch_one(const ResidentParams& p, int grid, hipStream_t s) {
-  const int bytes = lds_bytes(p.K);
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)q4_resident_kernel<SWIGLU, NST>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(kResidentMaxK));
-    attr = true;
-  }
-  hipLaunchKernelGGL((q4_resident_kernel<SWIGLU, NST>), dim3(grid), dim3(512), bytes, s, p);
+  hipLaunchKernelGGL((q4_resident_kernel<SWIGLU, NST>), dim3(grid), dim3(512), 0, s, p);
 }
 
 template <bool SWIGLU>

@@ -48,8 +48,6 @@
 // add to the matrix time instead of hiding under it.  Timing variants agree: without
 // any global load in the loop it still takes most of its time, and dropping the fold,
 // the unpacking or the LDS activation reads alone changes little.
-#include <stdlib.h>
-
 #include "common.h"
 #include "internal.h"
 #include "q4_stream.h"
@@ -88,7 +86,7 @@ __host__ __device__ inline int wide_unit_blocks(int NB, int NK) {
 // <= 512: 3 x 8 groups fit one MFMA); 0, per stage as an fp32 product over the stage's
 // four groups.
 template <bool SWIGLU, int GS, int BM>
-__device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& lds) {
+__device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& lds) {
   constexpr bool BB = BM != 0;
   constexpr int D = 2;  // weight register sets: the next stage's in flight
   const int tid = threadIdx.x, l = tid & 63;
@@ -516,7 +514,7 @@ __device__ __forceinline__ void wide_body(const TiledParams& p, const WideLds& l
 // GS: scale group of MFMA steps 0 and 1 after the word swaps, read off the swapped
 // word numbers on entry (both orders compiled).
 template <bool SWIGLU, int BM>
-__global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
+__global__ __launch_bounds__(512, 1) void q4_wide_kernel(WideParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char a0[A_BUF];
   __shared__ __attribute__((aligned(16))) unsigned char a1[A_BUF];
   __shared__ __attribute__((aligned(16))) unsigned char xp[XP_BYTES];
@@ -531,21 +529,15 @@ __global__ __launch_bounds__(512, 1) void q4_wide_kernel(TiledParams p) {
 }
 
 template <bool SWIGLU>
-void launch_w(TiledParams p, int64_t n_tiles_bound, hipStream_t s) {
+void launch_w(WideParams p, int64_t n_tiles_bound, int n_cu, hipStream_t s) {
   const int64_t bound = n_tiles_bound > 0 ? n_tiles_bound : 1;
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 0;
-  const int xc = ncu / 8;
+  const int xc = n_cu / 8;
   const int NB = SWIGLU ? (p.N >> 1) / 128 : p.N / 256;
   const int NUT = NB / wide_unit_blocks(NB, p.K / WKS);  // units per tile of a last round
   // workgroups per XCD: at most per + (xcd_cus - 1) (NUT - 1) for any tile count up to
   // the bound (per <= ceil(bound / 8): whole rounds, then at most xcd_cus - 1 tiles of NUT)
   const int64_t per_b = (bound + 7) / 8;
-  const char* env = getenv("MOEQ4_WIDE_SPLIT");  // "0": one workgroup per tile throughout
-  const bool split = !(env && env[0] == '0');
-  p.xcd_cus = split && xc >= 1 && per_b >= xc ? xc : 0;
+  p.xcd_cus = xc >= 1 && per_b >= xc ? xc : 0;
   const int64_t per_xcd = p.xcd_cus ? per_b + (int64_t)(xc - 1) * (NUT - 1) : per_b;
   // the bias once per block: with the 32 groups as k from four stages (16 groups) up,
   // with the pieces of X side by side in k up to two stages (8 groups)
@@ -562,9 +554,9 @@ bool wide_supported(int N, int K, bool swiglu, int a_rows) {
   return a_rows >= 1 && K > 0 && K % WKS == 0 && K <= kWideMaxK && N > 0 && N % 256 == 0;
 }
 
-void launch_wide(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s) {
-  if (swiglu) launch_w<true>(p, n_tiles_bound, s);
-  else launch_w<false>(p, n_tiles_bound, s);
+void launch_wide(WideParams p, bool swiglu, int64_t n_tiles_bound, int n_cu, hipStream_t s) {
+  if (swiglu) launch_w<true>(p, n_tiles_bound, n_cu, s);
+  else launch_w<false>(p, n_tiles_bound, n_cu, s);
 }
 
 }  // namespace moeq4

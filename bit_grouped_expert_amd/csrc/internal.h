@@ -13,11 +13,14 @@ void launch_router_split(const float* R, uint16_t* Rs, int E, int D, hipStream_t
 // the resident-tile GEMM
 void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T, int D, int E,
                           uint16_t* xprep, hipStream_t s);
-// Router logits L = x R^T (fp32): with T < 2048 and D % 256 == 0 on the fp32 matrix cores
-// from R directly, otherwise R split into three bf16 planes (Rs, 3 * ceil(E/16) * 16 * D)
-// and bf16 matrix cores.  xprep as above.
+// Router logits L = x R^T (fp32): with T <= 16 one wavefront per expert; with T < 2048
+// and D % 256 == 0 on the bf16 matrix cores with R split exactly in registers; otherwise
+// R split into three bf16 planes (Rs, 3 * ceil(E/16) * 16 * D) and bf16 matrix cores.
+// xprep as above.  planes_ready: Rs already holds the planes of this R (the split is
+// skipped).
+bool router_uses_planes(int T, int D);
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
-                   uint16_t* xprep, hipStream_t s);
+                   uint16_t* xprep, hipStream_t s, bool planes_ready = false);
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
                  float tau, int32_t* idx, float* w, hipStream_t s);
 
@@ -80,10 +83,6 @@ bool permute_small_ok(int T, int E);
 void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_tok, int32_t* slot_row, int shared_rows, int bm,
                           int4* tiles, int32_t* tile_count, hipStream_t s);
-// bm: 32 or 64 rows per tile.  Grid = max_tiles(rows_total, n_groups, bm) * n_slices.
-void launch_gemm_q4(GemmParams p, int bm, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
-int gemm_q4_slices(int N, bool swiglu);
-
 // Grouped engine for every group size: tiles of up to 32 rows (tile map built with
 // bm = 32), persistent XCD-aware grid of about 2 workgroups per compute unit.  Needs
 // p.xsum (row sums of A per 64-wide group); with SwiGLU it can also write the row sums
@@ -94,35 +93,10 @@ int grouped_slices(int N, bool swiglu);
 // out[r][g] = sum of A[r][64g .. 64g+63] in fp32, A bf16 [rows, K]
 void launch_row_group_sums(const uint16_t* A, int rows, int K, float* out, hipStream_t s);
 
-// Streamed engine (grouped_stream.hip): K % 128 == 0; A is the prepared copy (each
-// run of 8 columns stored in the order 0,4,1,5,2,6,3,7, one zero row after the
-// last, row a_rows) and xc holds per row and 128-K stage (-136 X_lo, -136 X_hi,
-// X_lo, X_hi) with X the row sums of the stage's two 64-wide groups.  Tiles of up to
-// 16 * nf rows (nf = 2 or 4; tile map built with bm = 16 * nf); one workgroup per
-// compute unit, persistent XCD-aware grid.
-struct StreamParams {
-  const uint16_t* A;          // prepared bf16 [a_rows + 1, K]
-  const float4* xc;           // [a_rows + 1, K / 128]
-  const int32_t* a_row_index; // nullable: identity
-  int32_t a_rows;             // >= 1
-  Q4Ptrs main;
-  int32_t n_main;
-  Q4Ptrs last;
-  int32_t N, K;
-  uint16_t* C;                // bf16 [rows, ldc]
-  int32_t ldc;
-  int32_t c_perm;             // store C in the prepared column order (SwiGLU only)
-  float4* xc_out;             // nullable; SwiGLU only: xc of C for the next GEMM
-  int32_t xc_out_ld;          // = (N / 2) / 128
-  const int4* tiles;
-  const int32_t* tile_count;
-  int32_t n_slices;
-};
-bool stream_supported(int N, int K, int a_rows);
-int stream_slices(int N, bool swiglu);
-void launch_prep(const uint16_t* A, int rows, int K, uint16_t* Ap, float4* xc, hipStream_t s);
-void launch_stream(StreamParams p, bool swiglu, int nf, int64_t n_tiles_bound, int n_cu,
-                   hipStream_t s);
+// The prepared copy of A read by the resident and wide engines: every run of 8 columns
+// stored in the order 0,4,1,5,2,6,3,7 (the order a packed word unpacks to), and one
+// zero row after the last (row `rows`), which rows outside [0, rows) read instead.
+void launch_prep(const uint16_t* A, int rows, int K, uint16_t* Ap, hipStream_t s);
 
 // Resident-tile engine (grouped_resident.hip), for small groups: tiles of up to 32
 // rows (tile map built with bm = 32) whose activation rows stay in LDS for the whole
@@ -159,15 +133,8 @@ struct ResidentPlan {
 bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, ResidentPlan* out);
 void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hipStream_t s);
 
-// Tiled engine (grouped_tiled.hip), for large groups: one workgroup per tile of up to
-// 128 rows (tile map built with bm = kTiledBM), walking every block of 256 weight rows
-// through LDS-staged 64-K stages.  A is the prepared copy (each run of 8 columns stored
-// in the order 0,4,1,5,2,6,3,7) and row a_rows of A must be readable and zero where a
-// row index can fall outside [0, a_rows).  Needs K % 256 == 0, N % 256 == 0 (SwiGLU:
-// N = 2F with F % 128 == 0) and a_rows >= 1; C rows are written with 8-byte stores
-// (ldc % 4 == 0).  With SwiGLU and c_perm set, C is stored in the prepared column order.
-constexpr int kTiledBM = 128;
-struct TiledParams {
+// Parameters of the wide-tile engine.
+struct WideParams {
   const uint16_t* A;          // prepared bf16 [a_rows (+1), K]
   const int32_t* a_row_index; // nullable: identity
   int32_t a_rows;
@@ -180,10 +147,8 @@ struct TiledParams {
   int32_t c_perm;
   const int4* tiles;
   const int32_t* tile_count;
-  int32_t xcd_cus;  // wide engine: compute units per XCD (set by launch_wide; 0: one tile each)
+  int32_t xcd_cus;  // compute units per XCD (set by launch_wide; 0: one tile per workgroup)
 };
-bool tiled_supported(int N, int K, bool swiglu, int a_rows);
-void launch_tiled(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
 
 // Wide-tile engine (grouped_wide.hip), for large groups: one workgroup per tile of up
 // to 128 rows (tile map built with bm = kWideBM), weights streamed into VGPRs, the
@@ -193,7 +158,7 @@ void launch_tiled(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t
 constexpr int kWideBM = 128;
 constexpr int kWideMaxK = 2048;
 bool wide_supported(int N, int K, bool swiglu, int a_rows);
-void launch_wide(TiledParams p, bool swiglu, int64_t n_tiles_bound, hipStream_t s);
+void launch_wide(WideParams p, bool swiglu, int64_t n_tiles_bound, int n_cu, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,

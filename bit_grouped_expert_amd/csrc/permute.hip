@@ -264,6 +264,12 @@ void launch_build_tiles(const int32_t* offsets, int n_groups, int rows_total, in
 }
 
 // ---------------------------------------------------------------------------- fused (T <= 1024)
+constexpr size_t small_lds(int E) {
+  return 16 * (size_t)E * 8 + 16 * (size_t)E * 4 + (size_t)(E + 2) * 4;
+}
+constexpr int kSmallMaxE = 768;  // above, the chunked kernels run
+static_assert(small_lds(kSmallMaxE) + 64 <= 160 * 1024, "LDS budget");
+
 // One workgroup of 1024 threads, thread t = token t: the histogram, the scan, the
 // stable scatter and the tile map of a small batch in one launch.  Same ranking as
 // the chunked kernels above: a token's rank among the tokens of expert e is the
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     int4* __restrict__ tiles, int cap, int32_t* __restrict__ tile_count) {
   // [16 waves][E] masks, then [16 waves][E] base rows (offset of the expert plus the
   // tokens of the lower waves), then offs[E + 2]
-  extern __shared__ unsigned long long masks[];
+  __shared__ unsigned long long masks[small_lds(kSmallMaxE) / 8];  // sized for the largest E
   int32_t* base = (int32_t*)(masks + 16 * E);
   int32_t* offs = base + 16 * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -337,11 +343,6 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   write_tiles(offs, n_groups, rows_total, bm, tiles, cap, tile_count, (int*)masks);
 }
 
-constexpr size_t small_lds(int E) {
-  return 16 * (size_t)E * 8 + 16 * (size_t)E * 4 + (size_t)(E + 2) * 4;
-}
-constexpr int kSmallMaxE = 768;  // above, the chunked kernels run
-static_assert(small_lds(kSmallMaxE) + 64 <= 160 * 1024, "LDS budget");
 
 bool permute_small_ok(int T, int E) { return T >= 1 && T <= 1024 && E <= kSmallMaxE; }
 
@@ -351,14 +352,7 @@ void launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* offs
   const int n_groups = E + (shared_rows >= 0 ? 1 : 0);
   const int rows_total = T * k + (shared_rows >= 0 ? shared_rows : 0);
   const int cap = (int)max_tiles(rows_total, n_groups, bm);
-  const size_t lds = small_lds(E);
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)permute_small_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)small_lds(kSmallMaxE));
-    attr = true;
-  }
-  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, idx, T, k, E, offsets,
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, idx, T, k, E, offsets,
                      sorted_tok, slot_row, shared_rows, bm, tiles, cap, tile_count);
 }
 

@@ -466,8 +466,12 @@ constexpr int kSmallTok = 16;  // the one-wavefront-per-expert kernel serves T <
 static void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
                                 uint16_t* xprep, hipStream_t s);
 
+bool router_uses_planes(int T, int D) {
+  return !(T <= kSmallTok && D % 256 == 0) && !(T < 2048 && D % kF32KC == 0);
+}
+
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
-                   uint16_t* xprep, hipStream_t s) {
+                   uint16_t* xprep, hipStream_t s, bool planes_ready) {
   if (T <= kSmallTok && D % 256 == 0) {
     launch_router_small(x, R, L, T, D, E, xprep, s);
     return;
@@ -478,7 +482,7 @@ void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, in
                        xprep);
     return;
   }
-  launch_router_split(R, Rs, E, D, s);
+  if (!planes_ready) launch_router_split(R, Rs, E, D, s);
   launch_router_logits(x, Rs, L, T, D, E, xprep, s);
 }
 
@@ -607,6 +611,65 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
     }
   }
 
+  // fp64 logits of up to four experts (uniform ids ce[0 .. nb-1]; slots past nb repeat
+  // ce[0]): lane d sums d, d + 64, ... in order (several steps of loads in flight), then a
+  // fixed butterfly adds the lanes, so every lane gets the four sums.  bf16 x fp32
+  // products are exact in fp64.
+  const uint16_t* xt = x + (int64_t)t * D;
+  auto exact4 = [&](const int* ce, int nb, double* out) __attribute__((always_inline)) {
+    const float* Rr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Rr[j] = R + (int64_t)(j < nb ? ce[j] : ce[0]) * D;
+    double sj[4] = {0.0, 0.0, 0.0, 0.0};
+    if constexpr (MAXC >= 16) {
+      // lane l takes d = 64 s + l of step s, two steps in flight (registers permitting)
+      constexpr int UN = 2;
+      for (int d0 = 0; d0 < D; d0 += 64 * UN) {
+        float xv[UN], rv[UN][4];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const int d = min(d0 + 64 * u + lane, D - 1);
+          xv[u] = d0 + 64 * u + lane < D ? bf16lo_to_f32(xt[d]) : 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rv[u][j] = Rr[j][d];
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sj[j] += (double)xv[u] * (double)rv[u][j];
+      }
+    } else {
+      // lane l takes d = 256 s + 4 l .. 4 l + 3 of step s (D % 64 == 0: a step's four d
+      // are all in range or all out), 16-byte loads of each row, four steps in flight
+      // (half the dependent rounds of single-element loads at the same registers per d)
+      constexpr int UN = 4;
+      for (int d0 = 0; d0 < D; d0 += 256 * UN) {
+        u32x2_t xv[UN];
+        f32x4_t rv[UN][4];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const int dd = d0 + 256 * u + 4 * lane;
+          const int d = dd < D ? dd : D - 4;
+          xv[u] = *(const u32x2_t*)(xt + d);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rv[u][j] = *(const f32x4_t*)(Rr[j] + d);
+          if (dd >= D) xv[u] = u32x2_t{0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const float xf[4] = {bf16lo_to_f32(xv[u][0]), bf16hi_to_f32(xv[u][0]),
+                               bf16lo_to_f32(xv[u][1]), bf16hi_to_f32(xv[u][1])};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sj[j] += (double)xf[c] * (double)rv[u][j][c];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = wave_sum_f64(sj[j]);
+  };
+
   if (k < E) {
     const float vk = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_v), k - 1));
     const float vk1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_v), k));
@@ -622,7 +685,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
       const int n_sure = __popcll(__ballot(lane < k && my_v >= thr_hi));
       double exact[MAXC];
       bool cand[MAXC];
-      const uint16_t* xt = x + (int64_t)t * D;
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = c * 64 + lane;
@@ -631,58 +693,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
       }
       int ce[4] = {0, 0, 0, 0}, nb = 0;  // expert ids of the pending batch (uniform)
       auto flush = [&]() __attribute__((always_inline)) {
-        const float* Rr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Rr[j] = R + (int64_t)(j < nb ? ce[j] : ce[0]) * D;
-        double sj[4] = {0.0, 0.0, 0.0, 0.0};
-        if constexpr (MAXC >= 16) {
-          // lane l takes d = 64 s + l of step s, two steps in flight (registers permitting)
-          constexpr int UN = 2;
-          for (int d0 = 0; d0 < D; d0 += 64 * UN) {
-            float xv[UN], rv[UN][4];
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-              const int d = min(d0 + 64 * u + lane, D - 1);
-              xv[u] = d0 + 64 * u + lane < D ? bf16lo_to_f32(xt[d]) : 0.f;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) rv[u][j] = Rr[j][d];
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) sj[j] += (double)xv[u] * (double)rv[u][j];
-          }
-        } else {
-        // lane l takes d = 256 s + 4 l .. 4 l + 3 of step s (D % 64 == 0: a step's four d
-        // are all in range or all out), 16-byte loads of each row, four steps in flight
-        // (half the dependent rounds of single-element loads at the same registers per d)
-        constexpr int UN = 4;
-        for (int d0 = 0; d0 < D; d0 += 256 * UN) {
-          u32x2_t xv[UN];
-          f32x4_t rv[UN][4];
-#pragma unroll
-          for (int u = 0; u < UN; ++u) {
-            const int dd = d0 + 256 * u + 4 * lane;
-            const int d = dd < D ? dd : D - 4;
-            xv[u] = *(const u32x2_t*)(xt + d);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) rv[u][j] = *(const f32x4_t*)(Rr[j] + d);
-            if (dd >= D) xv[u] = u32x2_t{0u, 0u};
-          }
-#pragma unroll
-          for (int u = 0; u < UN; ++u) {
-            const float xf[4] = {bf16lo_to_f32(xv[u][0]), bf16hi_to_f32(xv[u][0]),
-                                 bf16lo_to_f32(xv[u][1]), bf16hi_to_f32(xv[u][1])};
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) sj[j] += (double)xf[c] * (double)rv[u][j][c];
-          }
-        }
-        }
+        double sums[4];
+        exact4(ce, nb, sums);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const double sum = wave_sum_f64(sj[j]);
+          const double sum = sums[j];
           if (j < nb && (ce[j] & 63) == lane) {
 #pragma unroll
             for (int c = 0; c < MAXC; ++c)
@@ -728,6 +743,61 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
 #pragma unroll
           for (int c = 0; c < MAXC; ++c)
             if (c == (best.e >> 6)) cand[c] = false;
+        }
+      }
+    }
+  }
+
+  // The selected set is exact; so is its order wherever adjacent fp32 logits are at least
+  // tau apart.  Runs of selected experts whose neighbours are closer than that are
+  // rescored in fp64 and sorted within the run by (fp64 logit desc, expert id asc), with
+  // an odd-even transposition sort over the lanes of the run, so the order equals the
+  // exact descending order whenever the fp32 error is below tau / 2.
+  if (k > 1) {
+    const float vprev = __shfl(my_v, lane > 0 ? lane - 1 : 0);
+    const float vnext = __shfl(my_v, lane + 1 < 64 ? lane + 1 : 63);
+    const bool joins_prev = lane > 0 && lane < k && vprev - my_v < tau;
+    const bool joins_next = lane + 1 < k && my_v - vnext < tau;
+    uint64_t runs = __ballot(joins_prev || joins_next);
+    if (runs) {
+      const uint64_t breaks = ~__ballot(joins_prev);  // bit j: lane j starts a run
+      double ex = 0.0;
+      int ce[4] = {0, 0, 0, 0}, cl[4] = {0, 0, 0, 0}, nb = 0;
+      while (runs) {
+        const int b = __builtin_ctzll(runs);
+        runs &= runs - 1;
+        const int e = __builtin_amdgcn_readlane(my_e, b);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ce[j] = j == nb ? e : ce[j];
+          cl[j] = j == nb ? b : cl[j];
+        }
+        if (++nb == 4 || runs == 0) {
+          double sums[4];
+          exact4(ce, nb, sums);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j < nb && cl[j] == lane) ex = sums[j];
+          nb = 0;
+        }
+      }
+      for (int r = 0; r < k; ++r) {
+        const int partner = ((lane & 1) == (r & 1)) ? lane + 1 : lane - 1;
+        const int pl = partner < 0 ? 0 : (partner > 63 ? 63 : partner);
+        const double pv = __shfl(ex, pl);
+        const int pe = __shfl(my_e, pl);
+        const float pf = __shfl(my_v, pl);
+        const int hi = lane > partner ? lane : partner;
+        const bool same = partner >= 0 && partner < k && lane < k && !((breaks >> hi) & 1ull);
+        if (same) {
+          const Cand a{ex, my_e}, o{pv, pe};
+          // the lower lane keeps the better of the pair
+          const bool take = lane < partner ? better(o, a) : better(a, o);
+          if (take) {
+            ex = pv;
+            my_e = pe;
+            my_v = pf;
+          }
         }
       }
     }

@@ -55,3 +55,50 @@ def workspace(shp, device="cuda"):
     import torch
     n = _lib.moe_workspace_bytes(shp)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# ---- HIP timing events (raw handles), created without the system-scope fence that a default
+# event performs when it completes (a cache write-back and invalidate that slows the work after
+# it): these events only time.
+_HIP = None
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+
+def _hip():
+    """The HIP runtime that torch has already loaded."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        _HIP = ctypes.CDLL("libamdhip64.so")
+    return _HIP
+
+
+def hip_event() -> int:
+    """A timing HIP event without the system-scope fence on completion (raw handle)."""
+    import ctypes
+    e = ctypes.c_void_p()
+    rc = _hip().hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE))
+    if rc != 0:
+        raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+    return e.value
+
+
+def hip_event_record(e: int, stream) -> None:
+    import ctypes
+    rc = _hip().hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+
+def hip_elapsed_ms(a: int, b: int) -> float:
+    import ctypes
+    ms = ctypes.c_float()
+    rc = _hip().hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+    return ms.value
+
+
+def hip_event_destroy(e: int) -> None:
+    import ctypes
+    _hip().hipEventDestroy(ctypes.c_void_p(e))

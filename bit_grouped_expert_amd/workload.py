@@ -22,10 +22,13 @@ Recipe (all numpy PCG64):
                          codes: uniform random uint32 words [G, N, K/8], i.e. eight
                          independent uniform 4-bit codes per word;
                          scale = bf16_rne(|N(0, 0.02)|) [G, N, K/64];
-                         bias = bf16_rne(-scale * (7.5 + 0.5 z)), z = N(0, 1) per group
-                         (the bias of an affine 4-bit quantiser is the group's minimum,
-                         near -7.5 scales for normal weights; drawn per group, so it is
-                         not tied to the scale).
+                         bias, recipe "neg8" (the named workloads): bias = -8 * scale
+                         (exact in bf16), so w = (q - 8) * scale;
+                         bias, recipe "affine" (extra coverage): bias =
+                         bf16_rne(-scale * (7.5 + 0.5 z)), z = N(0, 1) per group, drawn
+                         after the scales (the bias of an affine 4-bit quantiser is the
+                         group's minimum, near -7.5 scales for normal weights; drawn per
+                         group, so it is not tied to the scale).
   skewed routing:        x[:, 0] = 1 and R[e, 0] = beta_e with
                          beta_e = -0.242 * ln(e+1) (Zipf-like popularity) and
                          beta_e = -1e4 for the last 4 experts (forced empty groups).
@@ -51,6 +54,7 @@ class MoEConfig:
     F: int          # expert d_ff (SwiGLU)
     routing: str = "natural"   # "natural" (random router) or "zipf" (biased router)
     n_layers: int = 1          # distinct weight sets run back to back on the same x
+    bias: str = "neg8"         # weight bias recipe: "neg8" (-8 * scale) or "affine"
 
     @property
     def G(self) -> int:
@@ -72,6 +76,11 @@ CONFIGS = {
     "uniform8192": MoEConfig("uniform8192", 8192, 2048, 256, 8, 512),
     # long-prompt chunk, four layers with distinct weights
     "long32768": MoEConfig("long32768", 32768, 2048, 256, 8, 512, n_layers=4),
+    # the same shapes with a free per-group bias (extra coverage of the bias arithmetic)
+    "tiny_affine": MoEConfig("tiny_affine", 16, 256, 16, 2, 128, bias="affine"),
+    "prefill512_affine": MoEConfig("prefill512_affine", 512, 2048, 256, 8, 512, bias="affine"),
+    "zipf8192_affine": MoEConfig("zipf8192_affine", 8192, 2048, 256, 8, 512, routing="zipf",
+                                 bias="affine"),
 }
 
 ZIPF_S = 1.1
@@ -129,13 +138,18 @@ def make_activations(cfg: MoEConfig, seed: int = 0):
     return x, router
 
 
-def _q4_matrix(rng, G, N, K):
+def _q4_matrix(rng, G, N, K, bias_recipe):
     assert K % GROUP == 0
     q = rng.integers(0, 2**32, size=(G, N, K // 8), dtype=np.uint32)
     s32 = np.abs(rng.standard_normal((G, N, K // GROUP), dtype=np.float32) * np.float32(0.02))
     scale = f32_to_bf16_bits(s32)
-    z = rng.standard_normal((G, N, K // GROUP), dtype=np.float32)
-    bias = f32_to_bf16_bits(-bf16_bits_to_f32(scale) * (np.float32(7.5) + np.float32(0.5) * z))
+    if bias_recipe == "neg8":
+        bias = f32_to_bf16_bits(np.float32(-8.0) * bf16_bits_to_f32(scale))
+    elif bias_recipe == "affine":
+        z = rng.standard_normal((G, N, K // GROUP), dtype=np.float32)
+        bias = f32_to_bf16_bits(-bf16_bits_to_f32(scale) * (np.float32(7.5) + np.float32(0.5) * z))
+    else:
+        raise ValueError(f"unknown bias recipe {bias_recipe!r}")
     return q, scale, bias
 
 
@@ -148,8 +162,8 @@ def make_weights(cfg: MoEConfig, seed: int = 1000) -> dict:
     """
     rng = _rng(seed)
     G, D, F = cfg.G, cfg.D, cfg.F
-    w1q, w1s, w1b = _q4_matrix(rng, G, 2 * F, D)
-    w2q, w2s, w2b = _q4_matrix(rng, G, D, F)
+    w1q, w1s, w1b = _q4_matrix(rng, G, 2 * F, D, cfg.bias)
+    w2q, w2s, w2b = _q4_matrix(rng, G, D, F, cfg.bias)
     return {
         "gate_up_q": w1q, "gate_up_s": w1s, "gate_up_b": w1b,
         "down_q": w2q, "down_s": w2s, "down_b": w2b,

@@ -14,12 +14,15 @@
  *   - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
  *     comment says otherwise; the caller owns every buffer.  The library
  *     allocates nothing, keeps no pointer after a call returns and has no
- *     mutable global state, so calls on different streams are thread-safe.
+ *     mutable global state (every launch decision is a function of the
+ *     arguments and of the current device), so calls on different streams with
+ *     different buffers are thread-safe.
  *   - Every compute call only enqueues work on `stream` (NULL = the legacy
  *     default stream) and never waits for the device; buffers must stay valid
  *     until the stream has passed the call.  No host synchronisation happens
  *     inside a call ([MTP] para. 6: routing stays on the GPU with no CPU sync
- *     inside the MoE layer).
+ *     inside the MoE layer).  No call enqueues a memset, so every compute call
+ *     may be captured into a HIP graph.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     nonzero status means nothing was enqueued.  MOE_ERR_LAUNCH reports a
  *     launch failure seen by hipGetLastError (kernels already enqueued by the
@@ -45,7 +48,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <hip/hip_runtime_api.h> /* hipStream_t */
+#include <hip/hip_runtime_api.h> /* hipStream_t, hipEvent_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -54,7 +57,8 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,      /* a required pointer is NULL */
-  MOE_ERR_SHAPE = 2,     /* a size is out of range or breaks a divisibility rule */
+  MOE_ERR_SHAPE = 2,     /* a size is out of range, breaks a divisibility rule, or an
+                            option names an engine that cannot take the shape */
   MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 4, /* the workspace is NULL or smaller than required */
   MOE_ERR_LAUNCH = 5,    /* a kernel launch failed (hipGetLastError) */
@@ -63,23 +67,51 @@ typedef enum {
 
 /* Layer shape.  T tokens, D = d_model, E routed experts, k experts per token,
  * F = expert d_ff.  Rules: 0 <= T; D % 64 == 0; F % 64 == 0; 1 <= E <= 1024;
- * 1 <= k <= min(E, 32); (k+1) * T * max(D, 2F) < 2^31. */
+ * 1 <= k <= min(E, 32); (k+1) * T * max(D, 2F) < 2^31.
+ * [MTP] para. 4 and [GF] "Requirements and model layout": 256 routed experts of
+ * which eight are picked per token, plus one shared expert. */
 typedef struct {
   int32_t T, d_model, n_experts, top_k, d_ff;
 } moe_shape;
 
-/* One packed 4-bit weight tensor (format above). */
+/* One packed 4-bit weight tensor (format above; [MTP] para. 5). */
 typedef struct {
   const uint32_t* q;
   const uint16_t* scale;
   const uint16_t* bias;
 } moe_q4;
 
-/* The weights of a set of SwiGLU experts, stored contiguously group after group. */
+/* The weights of a set of SwiGLU experts, stored contiguously group after group
+ * ([MTP] para. 5: the expert weights of the model are 4-bit groupwise affine). */
 typedef struct {
   moe_q4 gate_up; /* N = 2F, K = D */
   moe_q4 down;    /* N = D,  K = F */
 } moe_q4_ffn;
+
+/* Grouped-GEMM engine.  All compute the same result (see moe_grouped_gemm_q4); they
+ * differ in how rows and weights are tiled ([MTP] para. 6: the expert GEMMs walk tiles
+ * of expert rows through a block map).  AUTO picks from the shapes and the average
+ * group size; a forced engine that cannot take the shape gives MOE_ERR_SHAPE. */
+typedef enum {
+  MOE_ENGINE_AUTO = 0,
+  MOE_ENGINE_GROUPED = 1,  /* any N % 64, K % 64: tiles of up to 32 rows */
+  MOE_ENGINE_RESIDENT = 2, /* K % 256 == 0, K <= 2048: tiles of up to 32 rows held in LDS
+                              over the whole K while the weights stream (small groups) */
+  MOE_ENGINE_WIDE = 3      /* K % 256 == 0, K <= 2048, N % 256 == 0: tiles of up to 128
+                              rows (large groups) */
+} moe_engine;
+
+/* Options of moe_layer_forward_ex.  A NULL options pointer equals all fields zero. */
+#define MOE_N_STAGE_EVENTS 6
+typedef struct {
+  int32_t engine;     /* moe_engine used by both grouped GEMMs */
+  int32_t reserved;   /* must be 0 */
+  hipEvent_t* events; /* NULL, or MOE_N_STAGE_EVENTS caller-created events (entries may be
+                         NULL) recorded on `stream`: [0] before routing, [1] after routing
+                         (logits, top-k), [2] after the permutation and tile map, [3] after
+                         the grouped gate_up + SwiGLU, [4] after the grouped down, [5] after
+                         the combine */
+} moe_layer_opts;
 
 /* Byte offsets of the intermediates moe_layer_forward leaves in its workspace
  * (valid after the stream has passed the call, until the workspace is reused). */
@@ -97,15 +129,18 @@ typedef struct {
 /* Human-readable name of a status (static string; never NULL). */
 const char* moe_status_string(moe_status s);
 
-/* Workspace bytes moe_layer_forward needs for `shape`; this also covers
- * moe_route and moe_permute.  Host-only, pure; 0 if the shape is invalid. */
+/* Workspace bytes moe_layer_forward needs for `shape`; this also covers moe_route and
+ * moe_permute.  Host-only, pure; 0 if the shape is invalid.  [MTP] para. 6: the
+ * routing histogram, prefix scan, scatter and block map live in device memory that the
+ * layer's own GPU work reads (here, the caller's workspace). */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
-/* Fills `layout` for `shape`.  Host-only. */
+/* Fills `layout` for `shape`.  Host-only.  Same passage as moe_workspace_bytes. */
 moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout);
 
-/* Workspace bytes moe_grouped_gemm_q4 needs (its tile map and the per-64 row sums
- * of A).  Host-only, pure; 0 if the arguments are invalid. */
+/* Workspace bytes moe_grouped_gemm_q4 needs (its tile map, the per-64 row sums of A and
+ * a prepared copy of A).  Host-only, pure; 0 if the arguments are invalid.  [MTP]
+ * para. 6: the grouped GEMM is driven by a block map of expert-row tiles. */
 size_t moe_grouped_gemm_q4_workspace_bytes(int32_t n_groups, int32_t rows_total, int32_t a_rows,
                                            int32_t K);
 
@@ -124,7 +159,7 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* rou
 
 /* moe_route with an explicit near-tie threshold (moe_route uses 1e-4).  A larger
  * refine_gap sends more tokens through the exact fp64 rescoring (for testing);
- * refine_gap must be >= 0 (else MOE_ERR_SHAPE). */
+ * refine_gap must be >= 0 (else MOE_ERR_SHAPE).  [MTP] para. 4. */
 moe_status moe_route_ex(const moe_shape* shape, const uint16_t* x, const float* router_w,
                         int32_t* topk_idx, float* topk_w, float refine_gap, void* ws,
                         size_t ws_bytes, hipStream_t stream);
@@ -163,17 +198,26 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
  * the matrix cores from the exact values 128 + q and scaled in fp32, and the bias
  * part (b - 128 s) X (X: the row's sum over the group) comes from exact products of
  * b, s and X (X split into three bf16 pieces that sum to it exactly, or X itself in
- * fp32), so H is the fp32-accumulated product with the exactly dequantized weights.  The environment
- * variable MOEQ4_GEMM=rows selects an older engine with the same arithmetic (kept
- * for comparison). */
+ * fp32), so H is the fp32-accumulated product with the exactly dequantized weights. */
 moe_status moe_grouped_gemm_q4(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
                                const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
                                const int32_t* offsets, moe_q4 W, int32_t epilogue,
                                uint16_t* C, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_grouped_gemm_q4 with an explicit engine (moe_engine; MOE_ENGINE_AUTO is what
+ * moe_grouped_gemm_q4 uses).  Same results; an engine that cannot take the shape gives
+ * MOE_ERR_SHAPE.  [MTP] para. 5 (in-GEMM dequantization) and para. 6 (tiles of expert
+ * rows; 32-row tiles). */
+moe_status moe_grouped_gemm_q4_ex(int32_t n_groups, int32_t rows_total, int32_t N, int32_t K,
+                                  const uint16_t* A, int32_t a_rows, const int32_t* a_row_index,
+                                  const int32_t* offsets, moe_q4 W, int32_t epilogue,
+                                  uint16_t* C, void* ws, size_t ws_bytes, int32_t engine,
+                                  hipStream_t stream);
+
 /* Weighted combine: out[t] = bf16( S[t] + sum_j topk_w[t][j] * Y[slot_row[t*k+j]] ),
  * summed in fp32 (S = shared_out, or 0 when NULL).  slot_row entries outside
- * [0, T*k) are skipped.
+ * [0, T*k) are skipped.  [MTP] para. 4: each token's output joins its eight routed
+ * experts and the shared expert that sees every token.
  *   y_sorted bf16 [T*k, D]; slot_row int32 [T*k]; topk_w fp32 [T*k];
  *   shared_out bf16 [T, D] or NULL; out bf16 [T, D]. */
 moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const int32_t* slot_row,
@@ -182,7 +226,9 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const i
 
 /* The whole layer on one stream with no host synchronisation: route, permute,
  * grouped gate_up + SwiGLU over the E routed groups plus the shared expert as
- * one more group covering all T rows, grouped down, weighted combine.
+ * one more group covering all T rows, grouped down, weighted combine.  [MTP] para. 6
+ * (the routing stages stay in one GPU command stream with no CPU sync inside the MoE
+ * layer; expert GEMMs are most of prefill) and paras. 4-5.
  *   x bf16 [T, D]; router_w fp32 [E, D];
  *   experts: E groups (q [E, 2F, D/8] ... as in the weight format);
  *   shared: one group, or NULL for no shared expert; out bf16 [T, D];
@@ -191,17 +237,28 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const fl
                              const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* moe_layer_forward that also records caller-created HIP events on `stream` at
- * the stage boundaries, for per-stage timing: events[0] before routing,
- * [1] after routing (logits, top-k), [2] after the permutation and tile map,
- * [3] after the grouped gate_up + SwiGLU, [4] after the grouped down,
- * [5] after the combine.  `events` may be NULL and entries may be NULL
- * (skipped).  Same validation and results as moe_layer_forward. */
-#define MOE_N_STAGE_EVENTS 6
-moe_status moe_layer_forward_events(const moe_shape* shape, const uint16_t* x,
-                                    const float* router_w, const moe_q4_ffn* experts,
-                                    const moe_q4_ffn* shared, uint16_t* out, void* ws,
-                                    size_t ws_bytes, hipEvent_t* events, hipStream_t stream);
+/* moe_layer_forward with options (engine choice, stage events; NULL = defaults).  Same
+ * validation and results; opts->reserved must be 0 and opts->engine a moe_engine (else
+ * MOE_ERR_SHAPE).  [MTP] para. 6, as moe_layer_forward. */
+moe_status moe_layer_forward_ex(const moe_shape* shape, const uint16_t* x, const float* router_w,
+                                const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
+                                void* ws, size_t ws_bytes, const moe_layer_opts* opts,
+                                hipStream_t stream);
+
+/* Workspace bytes moe_layer_forward_chunked needs: that of one chunk of
+ * min(chunk_tokens, T) tokens.  Host-only, pure; 0 if the arguments are invalid. */
+size_t moe_chunked_workspace_bytes(const moe_shape* shape, int32_t chunk_tokens);
+
+/* The layer over T tokens in consecutive chunks of chunk_tokens (the last one shorter),
+ * each chunk one moe_layer_forward on the same stream with the same workspace, so the
+ * workspace is capped at one chunk's whatever T is ([MTP] para. 6: long prompts run in
+ * bounded chunks).  Results equal those of moe_layer_forward over all T tokens (routing
+ * and the expert FFNs act on each token alone).  chunk_tokens >= 1 (else MOE_ERR_SHAPE);
+ * ws >= moe_chunked_workspace_bytes(shape, chunk_tokens). */
+moe_status moe_layer_forward_chunked(const moe_shape* shape, const uint16_t* x,
+                                     const float* router_w, const moe_q4_ffn* experts,
+                                     const moe_q4_ffn* shared, uint16_t* out, int32_t chunk_tokens,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

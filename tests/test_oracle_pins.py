@@ -310,9 +310,16 @@ def test_generator_recipe():
     assert router.shape == (16, 256) and router.dtype == np.float32
     assert w["gate_up_q"].shape == (17, 256, 32) and w["gate_up_s"].shape == (17, 256, 4)
     assert w["down_q"].shape == (17, 256, 16) and w["down_s"].shape == (17, 256, 2)
-    s = oracle.bf16_to_f64(w["gate_up_s"])
-    b = oracle.bf16_to_f64(w["gate_up_b"])
-    assert np.all(s >= 0)
+    for key in ("gate_up", "down"):
+        s = oracle.bf16_to_f64(w[key + "_s"])
+        b = oracle.bf16_to_f64(w[key + "_b"])
+        assert np.all(s >= 0)
+        assert np.array_equal(b, -8 * s)  # the named workloads: bias = -8 * scale, exact
+    wa = wl.make_weights(wl.CONFIGS["tiny_affine"], 1000)
+    assert np.array_equal(wa["gate_up_q"], w["gate_up_q"])  # same codes and scales
+    assert np.array_equal(wa["gate_up_s"], w["gate_up_s"])
+    s = oracle.bf16_to_f64(wa["gate_up_s"])
+    b = oracle.bf16_to_f64(wa["gate_up_b"])
     ratio = -b[s > 0] / s[s > 0]          # bias = -scale * (7.5 + 0.5 z), bf16-rounded
     assert abs(ratio.mean() - 7.5) < 0.05 and 0.4 < ratio.std() < 0.6
     assert not np.array_equal(b, -8 * s)
