@@ -84,6 +84,9 @@ _SIGS = {
                                          C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32,
                                          C.c_void_p]),
     "moe_chunked_workspace_bytes": (C.c_size_t, [C.POINTER(moe_shape), C.c_int32]),
+    "moe_layer_forward_noalloc": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
+                                            C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn),
+                                            C.c_void_p, C.c_void_p]),
     "moe_layer_forward_chunked": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p,
                                             C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn),
                                             C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
@@ -244,3 +247,12 @@ def moe_layer_forward_chunked(shp, x, router_w, experts: moe_q4_ffn, shared, out
     _check(lib().moe_layer_forward_chunked(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
                                            _p(out), chunk_tokens, _p(ws), ws_bytes,
                                            _stream(stream)), "moe_layer_forward_chunked")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_layer_forward_noalloc(shp, x, router_w, experts: moe_q4_ffn, shared, out, stream=None):
+    sh = C.byref(shared) if shared is not None else None
+    _check(lib().moe_layer_forward_noalloc(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
+                                           _p(out), _stream(stream)), "moe_layer_forward_noalloc")

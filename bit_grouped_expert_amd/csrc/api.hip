@@ -5,6 +5,8 @@
 // the current device's compute-unit count.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moeq4.h"
 #include "internal.h"
 
@@ -218,6 +220,37 @@ void run_gemm(const GemmCall& c, const GemmPlan& plan, const ResidentPlan& rplan
     p.xsum_out_ld = c.N / 2 / 64;
     launch_grouped(p, swiglu, bound, n_cu, stream);
   }
+}
+
+// ---- scratch of moe_layer_forward_noalloc: a static device array (each GPU the library
+// runs on holds its own copy until the process ends).  In host code `scratch` is only a
+// stand-in for the symbol; its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];  // set once per device, then only read
+
+// The current device's address of `scratch` (taken on the first call on that device, with
+// that device current).
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    slot.ptr = slot.err == hipSuccess ? p : nullptr;
+  });
+  if (slot.err != hipSuccess || !slot.ptr) return MOE_ERR_DEVICE;
+  *out = slot.ptr;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -565,6 +598,22 @@ moe_status moe_layer_forward_ex(const moe_shape* shape, const uint16_t* x, const
                                 void* ws, size_t ws_bytes, const moe_layer_opts* opts,
                                 hipStream_t stream) {
   return layer_impl(shape, x, router_w, experts, shared, out, ws, ws_bytes, opts, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x,
+                                     const float* router_w, const moe_q4_ffn* experts,
+                                     const moe_q4_ffn* shared, uint16_t* out, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->T == 0) return MOE_OK;
+  if (make_layout(shape).total > kNoallocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MOE_OK) return st;
+  // nothing in the layer's workspace has to start at zero: every kernel writes what a later
+  // one reads (the prepared copy of x and its zero row included) before it is read
+  return layer_impl(shape, x, router_w, experts, shared, out, ws, kNoallocScratchBytes, nullptr,
+                    stream);
 }
 
 size_t moe_chunked_workspace_bytes(const moe_shape* shape, int32_t chunk_tokens) {

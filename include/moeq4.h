@@ -15,7 +15,9 @@
  *     comment says otherwise; the caller owns every buffer.  The library
  *     allocates nothing, keeps no pointer after a call returns and has no
  *     mutable global state (every launch decision is a function of the
- *     arguments and of the current device), so calls on different streams with
+ *     arguments and of the current device; the one exception is the device
+ *     address of moe_layer_forward_noalloc's scratch array, taken once per
+ *     device under std::call_once), so calls on different streams with
  *     different buffers are thread-safe.
  *   - Every compute call only enqueues work on `stream` (NULL = the legacy
  *     default stream) and never waits for the device; buffers must stay valid
@@ -259,6 +261,20 @@ moe_status moe_layer_forward_chunked(const moe_shape* shape, const uint16_t* x,
                                      const float* router_w, const moe_q4_ffn* experts,
                                      const moe_q4_ffn* shared, uint16_t* out, int32_t chunk_tokens,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): moe_layer_forward with no workspace argument.  The
+ * workspace is a static device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends (its address is taken once per device, on
+ * the first call there); the call allocates nothing.  A shape whose moe_workspace_bytes
+ * exceeds the array gives MOE_ERR_WORKSPACE (32 MiB: up to 580 tokens at d_model 2048,
+ * 256 experts top-8, d_ff 512).  Every call on one GPU shares that GPU's array and leaves
+ * its intermediates there: calls that overlap on one GPU (several streams or host
+ * threads) race and give undefined results.  Results equal moe_layer_forward's. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x,
+                                     const float* router_w, const moe_q4_ffn* experts,
+                                     const moe_q4_ffn* shared, uint16_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -153,3 +153,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         L.lib()
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """moe_layer_forward_noalloc checks the shape's workspace against its static scratch on the
+    host, before any HIP call: 1024 tokens of the 2048/256/8/512 layer need 53.6 MiB."""
+    big = shp(T=1024)
+    assert L.moe_workspace_bytes(big) > L.NOALLOC_SCRATCH_BYTES
+    q = L.q4(A, A, A)
+    ffn = L.q4_ffn(q, q)
+    assert lib.moe_layer_forward_noalloc(C.byref(big), A, A, C.byref(ffn), C.byref(ffn), A, None) \
+        == L.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_bytes(shp(T=512)) <= L.NOALLOC_SCRATCH_BYTES
+    bad = shp(D=100)
+    assert lib.moe_layer_forward_noalloc(C.byref(bad), A, A, C.byref(ffn), None, A, None) \
+        == L.MOE_ERR_SHAPE
