@@ -75,6 +75,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the layer: the grouped gate_up GEMM alone with n_e rows in "
+                         "each of the 257 groups, n_e = 1 .. 2048, per engine (regime evidence)")
+    ap.add_argument("--sweep-sizes", default="1,2,4,8,16,32,64,128,256,512,1024,2048")
+    ap.add_argument("--sweep-engines", default="resident,wide")
     return ap.parse_args()
 
 
@@ -255,6 +260,65 @@ def hbm_ceiling(torch, dev):
             "method": "torch copy_ of 1 GiB (read + write) and sum over 2 GiB, best of 5, HIP events"}
 
 
+def sweep(args, torch, L, dev, wl):
+    """The grouped gate_up + SwiGLU GEMM of the layer's shape (N = 2F = 1024, K = D = 2048,
+    257 groups: 256 experts and the shared one) with n_e rows in every group, for each engine:
+    one JSON line per (engine, n_e) with the call's time between two HIP events (it includes
+    the tile-map and prepared-copy launches; rocprofv3 gives the GEMM kernel alone), the
+    achieved HBM bandwidth on the algorithmic bytes and the achieved bf16 TFLOP/s."""
+    cfg = wl.CONFIGS["prefill512"]
+    G, N, K = cfg.E + 1, 2 * cfg.F, cfg.D
+    w = wl.make_weights(cfg, wl.layer_seed(0))
+    q = dev.to_device(w["gate_up_q"])
+    sc = dev.to_device(w["gate_up_s"])
+    bi = dev.to_device(w["gate_up_b"])
+    W = L.q4(q, sc, bi)
+    sizes = [int(v) for v in args.sweep_sizes.split(",")]
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = dev.hip_event(), dev.hip_event()
+    rng = np.random.default_rng(0)
+    for n_e in sizes:
+        rows = G * n_e
+        A = torch.from_numpy(wl.f32_to_bf16_bits(
+            rng.standard_normal((rows, K), dtype=np.float32)).view(np.int16)).cuda()
+        off = torch.arange(0, rows + 1, n_e, dtype=torch.int32, device="cuda")
+        C = torch.empty((rows, N // 2), dtype=torch.int16, device="cuda")
+        ws = torch.empty(L.moe_grouped_gemm_q4_workspace_bytes(G, rows, rows, K),
+                         dtype=torch.uint8, device="cuda")
+        wbytes = G * N * K * 0.5625
+        bytes_ = wbytes + rows * K * 2 + rows * (N // 2) * 2
+        flops = 2.0 * rows * N * K
+        for eng in args.sweep_engines.split(","):
+            def call():
+                L.moe_grouped_gemm_q4_ex(G, rows, N, K, A, rows, None, off, W, 1, C, ws, eng)
+            try:
+                for _ in range(3):
+                    call()
+            except L.MoEError as err:
+                log(f"sweep: {eng} n_e={n_e}: {err}")
+                continue
+            torch.cuda.synchronize()
+            reps = max(3, min(20, int(2e5 // max(rows, 1))))
+            ts = []
+            for _ in range(reps):
+                dev.hip_event_record(e0, stream)
+                call()
+                dev.hip_event_record(e1, stream)
+                torch.cuda.synchronize()
+                ts.append(dev.hip_elapsed_ms(e0, e1))
+            t = float(np.median(ts)) * 1e-3
+            rec = {"sweep": "grouped gate_up + SwiGLU, 257 groups, N=1024, K=2048",
+                   "engine": eng, "n_e": n_e, "rows": rows, "call_us": t * 1e6,
+                   "algorithmic_bytes": bytes_, "gbs": bytes_ / t / 1e9,
+                   "hbm_frac": bytes_ / t / 1e9 / HBM_PEAK_GBS,
+                   "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+                   "arith_intensity": flops / bytes_}
+            print(json.dumps(rec), flush=True)
+        del A, C, ws
+    dev.hip_event_destroy(e0)
+    dev.hip_event_destroy(e1)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -271,6 +335,9 @@ def main():
     cfg = wl.CONFIGS[args.config]
     assert torch.cuda.is_available()
     L.lib()
+    if args.sweep:
+        sweep(args, torch, L, dev, wl)
+        return
     log(f"bench: config {cfg.name} T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F}")
     host_w0 = None
     sets = []

@@ -48,6 +48,8 @@
 // add to the matrix time instead of hiding under it.  Timing variants agree: without
 // any global load in the loop it still takes most of its time, and dropping the fold,
 // the unpacking or the LDS activation reads alone changes little.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "q4_stream.h"
@@ -275,6 +277,104 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
       }
     }
   };
+  // The same stage, branch-free and software-pipelined, for NP fragment pairs (the tile's
+  // row fragments rounded up to pairs; rows past the tile repeat its last row and are
+  // dropped): 4 NP units (half hh, group g, fragment pair fp).  During unit u the wavefront
+  // issues the LDS reads of unit u + 1, the eight MFMAs of unit u and the folds of unit
+  // u - 1, and during the last unit of a group it also unpacks the next group's words, so
+  // that the LDS latency, the MFMA chains and the vector work overlap instead of following
+  // each other.  Same arithmetic, in the same order per output, as `compute`.
+  auto compute_pipe = [&](const StageW& w, const unsigned char* abuf, auto np_tag)
+                          __attribute__((always_inline)) {
+    constexpr int NP = decltype(np_tag)::value;
+    constexpr int NU = 4 * NP;
+    u32x4_t wsw[2];      // [weight fragment]: the current half's words after the swaps
+    u32x4_t Bq[2][2][2]; // [buffer][weight fragment][half step]
+    float sc[2][2];      // [buffer][weight fragment]
+    u32x4_t A[2][2][2];  // [buffer][fragment of the pair][half step]
+    f32x4_t P[2][2][2];  // [buffer][fragment of the pair][weight fragment]
+    auto unpack_group = [&](int hh, int g, int bb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) Bq[bb][j][h] = unpack_word(wsw[j][2 * (g ^ GS) + h], magic);
+        sc[bb][j] = g == 0 ? bf16lo_to_f32(w.s[j][hh]) : bf16hi_to_f32(w.s[j][hh]);
+      }
+    };
+    auto read_a = [&](int u, int ab) __attribute__((always_inline)) {
+      const int gi = u / NP, hh = gi >> 1, g = gi & 1, fp = u - gi * NP;
+      const unsigned char* base = abuf + hh * 4096;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          A[ab][e][h] = *(const u32x4_t*)(base + (2 * fp + e) * 8192 + a_step[2 * (g ^ GS) + h]);
+    };
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wsw[j] = swap_quad(w.c[j][0]);
+    unpack_group(0, 0, 0);
+    read_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int gi = u / NP, fp = u - gi * NP, cb = u & 1, bb = gi & 1;
+      if (u + 1 < NU) read_a(u + 1, cb ^ 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) P[cb][e][j] = mfma16x16x32(A[cb][e][0], Bq[bb][j][0], zero);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) P[cb][e][j] = mfma16x16x32(A[cb][e][1], Bq[bb][j][1], P[cb][e][j]);
+      if (u > 0) {
+        const int gq = (u - 1) / NP, fq = (u - 1) - gq * NP, pb = gq & 1;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[2 * fq + e][j][i] = fmaf(sc[pb][j], P[cb ^ 1][e][j][i], acc[2 * fq + e][j][i]);
+      }
+      const bool unpack_next = fp == NP - 1 && u + 1 < NU;
+      if (unpack_next) {
+        const int gn = gi + 1;
+        if ((gn >> 1) != (gi >> 1)) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) wsw[j] = swap_quad(w.c[j][1]);
+        }
+        unpack_group(gn >> 1, gn & 1, bb ^ 1);
+      }
+      // order inside the unit: the first MFMA (whose wait covers the reads issued a unit
+      // earlier), then this unit's four reads for the next unit, then each further MFMA
+      // followed by vector work (folds, and unpacking in a group's last unit)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u + 1 < NU) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (unpack_next) {
+#pragma unroll
+        for (int r = 0; r < 7; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 7; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the folds of the last unit (fragment pair NP - 1 of group 3: buffer 1)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[2 * (NP - 1) + e][j][i] = fmaf(sc[1][j], P[(NU - 1) & 1][e][j][i], acc[2 * (NP - 1) + e][j][i]);
+  };
   // X[row][group] of this wavefront's fragment for the stage's four groups: the product
   // of the group's two 32-K activation fragments with a fragment of ones (lanes of column
   // 0 hold it), stored as three bf16 pieces whose sum is X exactly (each takes the top
@@ -316,7 +416,7 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
   // (groups 8q .. 8q+7), loaded at the block's first stage as two 8-byte halves; a half
   // past K is loaded again from the row's first groups and not used.  BM 2: groups 0 .. 7
   // on every lane, taken from the stages' words as they stream (capture_sb).
-  const int sb_g0 = 8 * q;
+  const int sb_g0 = BM == 1 ? 8 * q : 0;
   const bool sb_lo = sb_g0 + 4 <= KG, sb_hi = sb_g0 + 8 <= KG;
   u32x2_t sbs[2][2], sbb[2][2];  // [weight fragment][half]
   auto load_sb = [&](int blk) __attribute__((always_inline)) {
@@ -478,37 +578,57 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
   // landed and a barrier publishes the next buffer.  The bias term of stage v follows
   // the barrier (X of a first block's stage is formed during it); after a block's last
   // stage its outputs, then the accumulators start over.
-  auto step = [&](int v, const unsigned char* cur_a, unsigned char* next_a, StageW& cur,
-                  StageW& fresh) __attribute__((always_inline)) {
-    const int vb = v / NK, st = v - vb * NK, blk = blk0 + vb;
-    const int vn = v + 1 < UT ? v + 1 : v;  // the last stage loads itself again
-    issue_a(vn - (vn / NK) * NK, next_a);
-    pf_load(fresh);
-    if (BM == 1 && st == 0) load_sb(blk);
-    float cbq[2];
-    compute(cur, cur_a, cbq);
-    if (BM == 2) capture_sb(st, cur);
-    // BM 1: after the workgroup's first block X is in LDS, and the block's bias product
-    // follows its first stage instead of delaying its end
-    if (BM == 1 && vb > 0 && st == 0) bias_block();
-    if (vb == 0) row_sums(st, cur_a);  // X during the first block of this workgroup
-    wait_vmcnt0();
-    lds_barrier();
-    if (!BB) bias_term(st, cbq);
-    if (st == NK - 1) {  // X of every group is in LDS from the first block's end
-      if (BM == 1 && vb == 0) bias_block();
-      if (BM == 2) bias_block_packed();
-      epilogue(blk);
-      reset();
-      if (BM == 2) clear_sb();
+  // The stage loop, one copy per stage form (NP > 0: the pipelined stage over NP fragment
+  // pairs; 0: the generic stage), chosen once per tile so that each copy keeps its own
+  // register allocation (a loop holding two forms spills).
+  auto run = [&](auto np_tag) __attribute__((always_inline)) {
+    constexpr int NP = decltype(np_tag)::value;
+    auto step = [&](int v, const unsigned char* cur_a, unsigned char* next_a, StageW& cur,
+                    StageW& fresh) __attribute__((always_inline)) {
+      const int vb = v / NK, st = v - vb * NK, blk = blk0 + vb;
+      const int vn = v + 1 < UT ? v + 1 : v;  // the last stage loads itself again
+      issue_a(vn - (vn / NK) * NK, next_a);
+      pf_load(fresh);
+      if (BB && st == 0) load_sb(blk);
+      float cbq[2];
+      if constexpr (NP > 0) compute_pipe(cur, cur_a, np_tag);
+      else compute(cur, cur_a, cbq);
+      // BM 1: after the workgroup's first block X is in LDS, and the block's bias product
+      // follows its first stage instead of delaying its end
+      if (BM == 1 && vb > 0 && st == 0) bias_block();
+      if (vb == 0) row_sums(st, cur_a);  // X during the first block of this workgroup
+      wait_vmcnt0();
+      lds_barrier();
+      if (!BB) bias_term(st, cbq);
+      if (st == NK - 1) {  // X of every group is in LDS from the first block's end
+        if (BM == 1 && vb == 0) bias_block();
+        if (BM == 2) {
+          take_sb();
+          bias_block_packed();
+        }
+        epilogue(blk);
+        reset();
+      }
+    };
+    int v = 0;
+    for (; v + 2 <= UT; v += 2) {
+      step(v, lds.a[0], lds.a[1], W[0], W[1]);
+      step(v + 1, lds.a[1], lds.a[0], W[1], W[0]);
     }
+    if (v < UT) step(v, lds.a[0], lds.a[1], W[0], W[1]);
   };
-  int v = 0;
-  for (; v + 2 <= UT; v += 2) {
-    step(v, lds.a[0], lds.a[1], W[0], W[1]);
-    step(v + 1, lds.a[1], lds.a[0], W[1], W[0]);
+  // K >= 1024 (bias once per block over 32 groups): the pipelined stage; the other forms
+  // (K <= 512, and the per-stage bias of K = 768) keep the generic stage, with which the
+  // pipelined form spills
+  if constexpr (BM == 1) {
+    const int np = (nfv + 1) >> 1;
+    if (np >= 4) run(std::integral_constant<int, 4>{});
+    else if (np == 3) run(std::integral_constant<int, 3>{});
+    else if (np == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
   }
-  if (v < UT) step(v, lds.a[0], lds.a[1], W[0], W[1]);
 }
 
 // GS: scale group of MFMA steps 0 and 1 after the word swaps, read off the swapped
