@@ -37,9 +37,9 @@ class moe_q4_ffn(C.Structure):
     _fields_ = [("gate_up", moe_q4), ("down", moe_q4)]
 
 
-MOE_ENGINE_AUTO, MOE_ENGINE_GROUPED, MOE_ENGINE_RESIDENT, MOE_ENGINE_WIDE = range(4)
+MOE_ENGINE_AUTO, MOE_ENGINE_GROUPED, MOE_ENGINE_RESIDENT, MOE_ENGINE_WIDE, MOE_ENGINE_DECODE = range(5)
 ENGINES = {"auto": MOE_ENGINE_AUTO, "grouped": MOE_ENGINE_GROUPED,
-           "resident": MOE_ENGINE_RESIDENT, "wide": MOE_ENGINE_WIDE}
+           "resident": MOE_ENGINE_RESIDENT, "wide": MOE_ENGINE_WIDE, "decode": MOE_ENGINE_DECODE}
 N_STAGE_EVENTS = 6
 
 

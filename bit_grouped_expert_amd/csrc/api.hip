@@ -69,6 +69,7 @@ bool plan_gemm(int32_t forced, int64_t rows, int n_groups, bool resident_ok, boo
 }
 
 bool engine_valid(int32_t e) { return e >= MOE_ENGINE_AUTO && e <= MOE_ENGINE_WIDE; }
+bool layer_engine_valid(int32_t e) { return e >= MOE_ENGINE_AUTO && e <= MOE_ENGINE_DECODE; }
 
 int device_cu_count() {
   int dev = 0, n = 0;
@@ -80,8 +81,17 @@ int device_cu_count() {
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, xsum_x, xsum_act, xprep, act, y, total;
+      tile_count, xsum_x, xsum_act, xprep, act, y, dec_plan, dec_act, total;
 };
+
+// slots of the decode-sized chain: the distinct touched experts and the shared expert
+int64_t decode_max_slots(const moe_shape* s) {
+  const int64_t pairs = (int64_t)s->T * s->top_k;
+  return (pairs < s->n_experts ? pairs : s->n_experts) + 1;
+}
+bool decode_ok(const moe_shape* s) {
+  return decode_supported(s->T, s->d_model, s->n_experts, s->top_k, s->d_ff);
+}
 
 Layout make_layout(const moe_shape* s) {
   const int64_t T = s->T, D = s->d_model, E = s->n_experts, k = s->top_k, F = s->d_ff;
@@ -108,6 +118,11 @@ Layout make_layout(const moe_shape* s) {
   L.xprep = take((T + 1) * D * 2);  // prepared x, one zero row after the last
   L.act = take((rows_ext + 1) * F * 2);
   L.y = take(rows_ext * D * 2);
+  L.dec_plan = L.dec_act = 0;
+  if (decode_ok(s)) {
+    L.dec_plan = take(decode_plan_bytes());
+    L.dec_act = take((size_t)decode_max_slots(s) * 16 * F * 2);
+  }
   L.total = o;
   return L;
 }
@@ -469,7 +484,8 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const int32_t engine = opts ? opts->engine : MOE_ENGINE_AUTO;
-  if (!engine_valid(engine) || (opts && opts->reserved != 0)) return MOE_ERR_SHAPE;
+  if (!layer_engine_valid(engine) || (opts && opts->reserved != 0)) return MOE_ERR_SHAPE;
+  if (engine == MOE_ENGINE_DECODE && !decode_ok(shape)) return MOE_ERR_SHAPE;
   if (shape->T == 0) return MOE_OK;
   if (!x || !router_w || !experts || !out) return MOE_ERR_NULL;
   if (!q4_ok(experts->gate_up) || !q4_ok(experts->down)) return MOE_ERR_NULL;
@@ -487,6 +503,50 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   const bool has_shared = shared != nullptr;
   const int n_groups = E + (has_shared ? 1 : 0);
   const int rows = T * k + (has_shared ? T : 0);
+
+  hipEvent_t* events = opts ? opts->events : nullptr;
+  bool event_failed = false;
+  auto mark = [&](int i) {
+    if (events && events[i] && hipEventRecord(events[i], stream) != hipSuccess) event_failed = true;
+  };
+  auto finish = [&]() {
+    const moe_status ls = launch_status();
+    return ls != MOE_OK ? ls : (event_failed ? MOE_ERR_LAUNCH : MOE_OK);
+  };
+
+  if (engine == MOE_ENGINE_DECODE || (engine == MOE_ENGINE_AUTO && decode_ok(shape))) {
+    // decode-sized chain: router logits (+ prepared x), plan, gate_up + SwiGLU, down + combine
+    uint16_t* xprep = at<uint16_t>(ws, L.xprep);
+    void* plan = at<void>(ws, L.dec_plan);
+    mark(0);
+    launch_router(x, router_w, at<uint16_t>(ws, L.rsplit), at<float>(ws, L.logits), T, D, E, xprep,
+                  stream, planes_ready);
+    launch_decode_plan(at<float>(ws, L.logits), x, router_w, T, D, E, k, kRefineGap, has_shared,
+                       at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_w),
+                       at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_tok),
+                       at<int32_t>(ws, L.slot_row), plan, stream);
+    mark(1);
+    mark(2);
+    DecodeParams dp;
+    memset(&dp, 0, sizeof(dp));
+    dp.T = T;
+    dp.D = D;
+    dp.F = F;
+    dp.xprep = xprep;
+    dp.plan = plan;
+    dp.act = at<uint16_t>(ws, L.dec_act);
+    dp.out = out;
+    dp.up_main = q4p(experts->gate_up);
+    dp.down_main = q4p(experts->down);
+    dp.up_last = has_shared ? q4p(shared->gate_up) : dp.up_main;
+    dp.down_last = has_shared ? q4p(shared->down) : dp.down_main;
+    launch_decode_gate_up(dp, (int)decode_max_slots(shape) - (has_shared ? 0 : 1), stream);
+    mark(3);
+    launch_decode_down_combine(dp, stream);
+    mark(4);
+    mark(5);
+    return finish();
+  }
 
   // the GEMM engine depends only on the shapes: chosen first, so that the router can
   // write the prepared copy of x on the way
@@ -515,11 +575,6 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   float* xsum_act = at<float>(ws, L.xsum_act);
   uint16_t* xprep = at<uint16_t>(ws, L.xprep);
 
-  hipEvent_t* events = opts ? opts->events : nullptr;
-  bool event_failed = false;
-  auto mark = [&](int i) {
-    if (events && events[i] && hipEventRecord(events[i], stream) != hipSuccess) event_failed = true;
-  };
   // routing (the router also writes the prepared copy of x)
   mark(0);
   launch_router(x, router_w, at<uint16_t>(ws, L.rsplit), at<float>(ws, L.logits), T, D, E,
@@ -583,8 +638,7 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   launch_combine(y, (int64_t)T * k, slot_row, wts, has_shared ? y + (int64_t)T * k * D : nullptr,
                  out, T, D, k, stream);
   mark(5);
-  const moe_status ls = launch_status();
-  return ls != MOE_OK ? ls : (event_failed ? MOE_ERR_LAUNCH : MOE_OK);
+  return finish();
 }
 
 moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const float* router_w,

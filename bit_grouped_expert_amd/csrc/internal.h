@@ -160,6 +160,30 @@ constexpr int kWideMaxK = 2048;
 bool wide_supported(int N, int K, bool swiglu, int a_rows);
 void launch_wide(WideParams p, bool swiglu, int64_t n_tiles_bound, int n_cu, hipStream_t s);
 
+// ---------------------------------------------------------------- decode-sized layer
+// T <= 16 tokens (decode.hip): plan (top-k, touched-expert slots, combine weights, routing
+// outputs), gate_up + SwiGLU per (slot, 16-row slice), down fused with the combine per 16
+// output columns.  No permuted rows, no expert-output array.
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxPairs = 128;                  // T * k
+constexpr int kDecodeMaxSlots = kDecodeMaxPairs + 1;  // distinct experts + the shared one
+struct DecodeParams {
+  int32_t T, D, F;
+  const uint16_t* xprep;  // prepared x [T + 1, D], row T zero
+  void* plan;             // decode_plan_bytes() bytes
+  uint16_t* act;          // bf16 [max slots][16][F], prepared column order
+  uint16_t* out;          // bf16 [T, D]
+  Q4Ptrs up_main, up_last, down_main, down_last;  // experts [E, ...]; the shared expert
+};
+bool decode_supported(int T, int D, int E, int k, int F);
+size_t decode_plan_bytes();
+void launch_decode_plan(const float* L, const uint16_t* x, const float* R, int T, int D, int E,
+                        int k, float tau, bool has_shared, int32_t* idx, float* w,
+                        int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, void* plan,
+                        hipStream_t s);
+void launch_decode_gate_up(const DecodeParams& p, int max_slots, hipStream_t s);
+void launch_decode_down_combine(const DecodeParams& p, hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,
                     const uint16_t* S, uint16_t* out, int T, int D, int k, hipStream_t s);

@@ -99,8 +99,11 @@ typedef enum {
   MOE_ENGINE_GROUPED = 1,  /* any N % 64, K % 64: tiles of up to 32 rows */
   MOE_ENGINE_RESIDENT = 2, /* K % 256 == 0, K <= 2048: tiles of up to 32 rows held in LDS
                               over the whole K while the weights stream (small groups) */
-  MOE_ENGINE_WIDE = 3      /* K % 256 == 0, K <= 2048, N % 256 == 0: tiles of up to 128
+  MOE_ENGINE_WIDE = 3,     /* K % 256 == 0, K <= 2048, N % 256 == 0: tiles of up to 128
                               rows (large groups) */
+  MOE_ENGINE_DECODE = 4    /* moe_layer_forward_ex only: the decode-sized chain (T <= 16,
+                              T * k <= 128, d_model % 256 == 0; the automatic choice there):
+                              no permuted rows, the down product fused with the combine */
 } moe_engine;
 
 /* Options of moe_layer_forward_ex.  A NULL options pointer equals all fields zero. */
@@ -123,8 +126,10 @@ typedef struct {
   size_t offsets;    /* int32 [E + 2]  group row offsets; [E+1] = (k+1)T (shared group) */
   size_t sorted_tok; /* int32 [(k+1)T] token of each permuted row (tail: 0..T-1) */
   size_t slot_row;   /* int32 [T, k]   permuted row of pair (t, j) */
-  size_t act;        /* bf16  [(k+1)T, F] SwiGLU activations, permuted rows */
-  size_t y;          /* bf16  [(k+1)T, D] expert outputs; rows kT.. = shared expert */
+  size_t act;        /* bf16  [(k+1)T, F] SwiGLU activations, permuted rows (not written
+                        by the decode-sized chain) */
+  size_t y;          /* bf16  [(k+1)T, D] expert outputs; rows kT.. = shared expert (not
+                        written by the decode-sized chain, which never stores them) */
   size_t total;      /* == moe_workspace_bytes */
 } moe_ws_layout;
 

@@ -568,3 +568,97 @@ def test_layer_stage_events(torch_cuda):
     for e in evs:
         dev.hip_event_destroy(e)
     assert np.array_equal(dev.to_host(out, np.uint16), plain)
+
+
+# ----------------------------------------------------------------------------- decode sizes
+DECODE_SHAPES = [(1, 2048, 256, 8, 512), (4, 2048, 256, 8, 512), (16, 2048, 256, 8, 512),
+                 (4, 256, 1000, 32, 128), (3, 512, 40, 8, 64), (16, 256, 16, 2, 128)]
+
+
+@pytest.mark.parametrize("engine", ["decode", "resident"])
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_layer_decode_sizes(torch_cuda, shape, engine):
+    """T <= 16: the decode-sized chain (plan, gate_up per slot and slice, down fused with the
+    combine) and the grouped chain on the same layers, every element against the oracle and
+    the routing outputs (ordered top-k, offsets, permuted rows) on every token.  Shapes: the
+    Qwen-like layer at 1, 4 and 16 tokens (16 x 8 = 128 pairs, the most the chain takes),
+    k = 32 with 1000 experts (128 pairs, E > 256), F = 64 (one 64-wide group per down row)."""
+    T, D, E, k, F = shape
+    cfg = wl.MoEConfig("dec", T, D, E, k, F)
+    x, router = wl.make_activations(cfg, 11)
+    w = wl.make_weights(cfg, 99)
+    lw = dev.LayerWeights(w, cfg.E)
+    say(f"decode-sized layer {shape} [{engine}]")
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw, engine=engine)
+    _check_layer_integer_stages(cfg, x, router, inter)
+    ref = oracle.moe_layer(x, router, w, cfg.k)
+    check_tol(bf16f(got), ref["out"], f"decode-sized layer {shape} [{engine}]")
+
+
+def test_layer_decode_no_shared(torch_cuda):
+    cfg = wl.MoEConfig("dec_ns", 4, 2048, 256, 8, 512)
+    x, router = wl.make_activations(cfg, 12)
+    w = wl.make_weights(cfg, 98)
+    lw = dev.LayerWeights(w, cfg.E)
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw, with_shared=False, engine="decode")
+    _check_layer_integer_stages(cfg, x, router, inter, with_shared=False)
+    ref = oracle.moe_layer(x, router, w, cfg.k, with_shared=False)
+    check_tol(bf16f(got), ref["out"], "decode-sized layer without the shared expert")
+
+
+def test_decode_engine_rejects_large_batches(torch_cuda):
+    cfg = wl.MoEConfig("dec_big", 17, 2048, 256, 8, 512)
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    x, router = wl.make_activations(cfg, 0)
+    lw = dev.LayerWeights(wl.make_weights(cfg, 1000), cfg.E)
+    out = torch_cuda.empty((cfg.T, cfg.D), dtype=torch_cuda.int16, device="cuda")
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_forward_ex(shp, dev.to_device(x), dev.to_device(router), lw.experts,
+                               lw.shared, out, dev.workspace(shp), L.layer_opts("decode"))
+    assert ei.value.status == L.MOE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode4"])
+def test_layer_decode_graph_replay(torch_cuda, name):
+    """The decode-sized layer captured into a HIP graph (torch.cuda.CUDAGraph) and replayed
+    five times with new inputs copied in and eager work between replays: every replay equals
+    the eager call on the same inputs, bit for bit."""
+    torch = torch_cuda
+    cfg = wl.CONFIGS[name]
+    lw = dev.LayerWeights(wl.make_weights(cfg, wl.layer_seed(0)), cfg.E)
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    xs, rs = [], []
+    for seed in range(5):
+        x, r = wl.make_activations(cfg, seed)
+        xs.append(dev.to_device(x))
+        rs.append(dev.to_device(r))
+    xin, rin = torch.empty_like(xs[0]), torch.empty_like(rs[0])
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
+    # eager references
+    refs = []
+    for i in range(5):
+        o = torch.empty_like(out)
+        L.moe_layer_forward(shp, xs[i], rs[i], lw.experts, lw.shared, o, ws)
+        refs.append(o)
+    torch.cuda.synchronize()
+    xin.copy_(xs[0])
+    rin.copy_(rs[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # one warm call on the side stream before capture
+        L.moe_layer_forward(shp, xin, rin, lw.experts, lw.shared, out, ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.moe_layer_forward(shp, xin, rin, lw.experts, lw.shared, out, ws)
+    for i in range(5):
+        xin.copy_(xs[i])
+        rin.copy_(rs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[i]), f"replay {i} differs from the eager call"
+        junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
