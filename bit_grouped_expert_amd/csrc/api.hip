@@ -81,7 +81,7 @@ int device_cu_count() {
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, xsum_x, xsum_act, xprep, act, y, dec_plan, dec_act, total;
+      tile_count, xsum_x, xsum_act, xprep, act, y, dec_sync, dec_part, dec_act, total;
 };
 
 // slots of the decode-sized chain: the distinct touched experts and the shared expert
@@ -90,7 +90,8 @@ int64_t decode_max_slots(const moe_shape* s) {
   return (pairs < s->n_experts ? pairs : s->n_experts) + 1;
 }
 bool decode_ok(const moe_shape* s) {
-  return decode_supported(s->T, s->d_model, s->n_experts, s->top_k, s->d_ff);
+  return decode_supported(s->T, s->d_model, s->n_experts, s->top_k, s->d_ff) &&
+         router_small_ok(s->T, s->d_model);
 }
 
 Layout make_layout(const moe_shape* s) {
@@ -118,10 +119,12 @@ Layout make_layout(const moe_shape* s) {
   L.xprep = take((T + 1) * D * 2);  // prepared x, one zero row after the last
   L.act = take((rows_ext + 1) * F * 2);
   L.y = take(rows_ext * D * 2);
-  L.dec_plan = L.dec_act = 0;
+  L.dec_sync = L.dec_part = L.dec_act = 0;
   if (decode_ok(s)) {
-    L.dec_plan = take(decode_plan_bytes());
-    L.dec_act = take((size_t)decode_max_slots(s) * 16 * F * 2);
+    const int ms = (int)decode_max_slots(s);
+    L.dec_sync = take((size_t)decode_sync_ints((int)D, (int)F, ms) * 4);
+    L.dec_part = take(decode_part_bytes((int)D, (int)F, ms));
+    L.dec_act = take(decode_act_bytes((int)F, ms));
   }
   L.total = o;
   return L;
@@ -515,34 +518,44 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   };
 
   if (engine == MOE_ENGINE_DECODE || (engine == MOE_ENGINE_AUTO && decode_ok(shape))) {
-    // decode-sized chain: router logits (+ prepared x), plan, gate_up + SwiGLU, down + combine
-    uint16_t* xprep = at<uint16_t>(ws, L.xprep);
-    void* plan = at<void>(ws, L.dec_plan);
+    // decode-sized chain: router logits (+ prepared x, + the counters cleared), then one
+    // persistent launch: plan, gate_up + SwiGLU, down + combine
+    int32_t* sync = at<int32_t>(ws, L.dec_sync);
     mark(0);
-    launch_router(x, router_w, at<uint16_t>(ws, L.rsplit), at<float>(ws, L.logits), T, D, E, xprep,
-                  stream, planes_ready);
-    launch_decode_plan(at<float>(ws, L.logits), x, router_w, T, D, E, k, kRefineGap, has_shared,
-                       at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_w),
-                       at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_tok),
-                       at<int32_t>(ws, L.slot_row), plan, stream);
+    launch_router_small(x, router_w, at<float>(ws, L.logits), T, D, E, at<uint16_t>(ws, L.xprep),
+                        sync, decode_sync_ints(D, F, (int)decode_max_slots(shape)), stream);
     mark(1);
     mark(2);
     DecodeParams dp;
     memset(&dp, 0, sizeof(dp));
     dp.T = T;
     dp.D = D;
+    dp.E = E;
+    dp.k = k;
     dp.F = F;
-    dp.xprep = xprep;
-    dp.plan = plan;
+    dp.has_shared = has_shared ? 1 : 0;
+    dp.group_slots = decode_group_slots(F);
+    dp.n_cb = D / 16;
+    dp.tau = kRefineGap;
+    dp.logits = at<float>(ws, L.logits);
+    dp.x = x;
+    dp.R = router_w;
+    dp.xprep = at<uint16_t>(ws, L.xprep);
+    dp.idx = at<int32_t>(ws, L.topk_idx);
+    dp.w = at<float>(ws, L.topk_w);
+    dp.offsets = at<int32_t>(ws, L.offsets);
+    dp.sorted_tok = at<int32_t>(ws, L.sorted_tok);
+    dp.slot_row = at<int32_t>(ws, L.slot_row);
+    dp.sync = sync;
+    dp.part = at<float>(ws, L.dec_part);
     dp.act = at<uint16_t>(ws, L.dec_act);
     dp.out = out;
     dp.up_main = q4p(experts->gate_up);
     dp.down_main = q4p(experts->down);
     dp.up_last = has_shared ? q4p(shared->gate_up) : dp.up_main;
     dp.down_last = has_shared ? q4p(shared->down) : dp.down_main;
-    launch_decode_gate_up(dp, (int)decode_max_slots(shape) - (has_shared ? 0 : 1), stream);
+    launch_decode_layer(dp, (int)decode_max_slots(shape) - (has_shared ? 0 : 1), stream);
     mark(3);
-    launch_decode_down_combine(dp, stream);
     mark(4);
     mark(5);
     return finish();

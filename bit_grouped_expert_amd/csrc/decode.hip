@@ -1,34 +1,46 @@
-// The MoE layer at decode sizes (T <= 16 tokens): a launch chain whose kernels spread the
-// few touched experts' weights over every compute unit, with no permutation of token rows
-// and no expert-output array in memory.
+// The MoE layer at decode sizes (T <= 16 tokens): one persistent launch after the router
+// logits, whose workgroups stream the few touched experts' weights on every compute unit,
+// with no permutation of token rows and no expert-output array in memory.
 //
 // Pages: MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference engine for
 // Qwen3.6-35B-A3B on Apple Silicon", body paragraph 7 (batch-1 decode reuses almost no
 // weight, so memory bandwidth is the ceiling, and the engine cuts the number of sequential
-// kernel stages) and paragraph 4 (eight of 256 experts per token plus a shared expert).
+// kernel stages by running independent kernels together) and paragraph 4 (eight of 256
+// experts per token plus a shared expert).
 //
-// Chain (after the router logits, computed by the one-wavefront-per-expert router kernel,
-// which also writes the prepared copy of x with a zero row after the last token):
-//   plan          one workgroup: the top k of every token (exact, the router's own
-//                 selection code), the sorted list of distinct touched experts ("slots",
-//                 the shared expert last), each slot's combine weight for each token, and
-//                 the layer's routing outputs (top-k, group offsets, permuted rows);
-//   gate_up       one workgroup per (slot, 16 weight rows of gate and the matching 16 of
-//                 up): the 16-row fragment of all tokens (rows past T are the zero row)
-//                 against those rows, K split over four wavefronts, SwiGLU, activations
-//                 stored per slot;
-//   down+combine  one workgroup per 16 output columns: every (slot, 64-wide group) unit
-//                 of the down product for those columns, scaled by the slot's combine
-//                 weight per token and summed in fp32 in a fixed order, so the expert
-//                 outputs never leave registers.
+// The launch (after the one-wavefront-per-expert router, which also writes the prepared
+// copy of x and clears this launch's counters):
+//   plan      every workgroup: the top k of every token (exact, the router's own selection
+//             code), the sorted list of distinct touched experts ("slots", the shared
+//             expert last), each slot's combine weight and token mask; workgroup 0 also
+//             writes the layer's routing outputs (top-k, group offsets, permuted rows);
+//   items     one per workgroup, in workgroup order, gate_up items first:
+//     gate_up  (slot, 16 rows of gate and the matching 16 of up): the slot's tokens
+//              against those rows, K over eight wavefronts, SwiGLU, activations stored
+//              in the down step's fragment order; then the slot's counter is raised;
+//     down     (16 output columns, group of consecutive slots): the group's down weights
+//              are staged first, then the item waits for its slots' gate_up counters,
+//              multiplies, scales by the combine weights and sums in fp32 in a fixed
+//              order; with several groups the last one to arrive adds the groups'
+//              partial sums in group order and writes the bf16 output.
+// A down item waits only on gate_up items, all of lower workgroup index.  Workgroups are
+// dispatched in index order, so those are running or done, and they never wait: every
+// wait ends, whether or not the whole grid fits on the chip at once.  A wait is also
+// bounded: past the limit it raises the error word and goes on.
+//
+// Cross-workgroup data (activations, the groups' partial sums) and the counters use
+// device-scope loads and stores, which are coherent across the chiplets' L2 caches without
+// cache-wide write-back or invalidation; a writer waits for its stores to complete before
+// it raises a counter, and a reader loads only after it has seen the counter.  A single
+// counter that every workgroup increments (a ticket queue) serialises at the memory and
+// costs far more than a whole item, so items are not dealt that way.
 //
 // Arithmetic per 64-wide group g of one weight row (scale s, bias b): the matrix cores give
 // P' = sum x (128 + q) with exact products (128 + q is the bf16 0x4300 | q) and the row sums
 // X = sum x (activations times a fragment of ones); then acc += s P' + (b - 128 s) X in
 // fp32.  The K order inside a group is a permutation shared by both operands: in MFMA step
 // h of group g, quarter q of the lanes takes packed word 8 g + 2 q + h of its weight row
-// and the matching eight activations, so each step stays inside one scale group and a lane
-// loads its two words of a group with one 8-byte load.
+// and the matching eight activations, so each step stays inside one scale group.
 #include "common.h"
 #include "internal.h"
 #include "q4_stream.h"
@@ -38,107 +50,79 @@ namespace moeq4 {
 
 namespace {
 
-// the ws pieces of the plan
-struct PlanPtrs {
-  int32_t* n_slots;      // [1]
-  int32_t* slot_expert;  // [max_slots]: expert id, -1 = the shared expert
-  float* coef;           // [max_slots][16]: combine weight of the slot for token t
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kUpMaxD = 2048;
+constexpr int kMaxF = 1024;
+constexpr int kGroupSlots = 10;                       // most slots of one down item
+constexpr int kDownCodeArea = 40 * 1024;              // code slices of one down item
+constexpr int kDownSbArea = kDownCodeArea / 8;        // their scales and biases
+constexpr int kDownActArea = 16 * 1024;               // activation rows of one round
+constexpr int kUpCodeBytes = 32 * kUpMaxD / 2;        // 32 code rows of one gate_up item
+constexpr int kUpSbBytes = 4 * 32 * (kUpMaxD / 64);   // their scales and biases
+constexpr int kSlack = 1024;                          // past-the-end writes of staging
+constexpr int kUpArea = kUpCodeBytes + kSlack + kUpSbBytes + kSlack;
+constexpr int kDownArea = kDownCodeArea + kSlack + kDownSbArea + kSlack + kDownActArea + kSlack;
+constexpr int kArea = kUpArea > kDownArea ? kUpArea : kDownArea;
+constexpr int kSpinLimit = 1 << 16;                   // polls before a wait gives up
+static_assert((int)sizeof(f32x4_t) * kWaves * 2 * 64 <= kUpCodeBytes, "gate_up reduction");
+static_assert((int)sizeof(float) * kWaves * 16 * 17 <= kDownCodeArea, "down reduction");
+static_assert(kGroupSlots <= 16, "pair scan width");
+
+// counters and flags, cleared before every launch: [0] error (waits that gave up);
+// [kSyncCb + 32 cb] down groups done for column block cb, one 128-byte line each; then one
+// done flag per gate_up item, slot-major, set by a plain store.  Many atomics on one line
+// serialise at the memory, so nothing is counted that way on the critical path.
+constexpr int kSyncCb = 32;
+__host__ __device__ inline int sync_flags_base(int n_cb) { return kSyncCb + 32 * n_cb; }
+
+// the plan, in LDS, identical in every workgroup
+struct Plan {
+  float coef[kDecodeMaxSlots * 16];   // combine weight of slot s for token t (16-byte rows)
+  int sel_e[kDecodeMaxPairs];
+  float sel_w[kDecodeMaxPairs];
+  uint32_t bits[32];  // touched experts, E <= 1024
+  int word_base[33];
+  int slot_exp[kDecodeMaxSlots];      // expert of each slot, -1 = the shared expert
+  uint32_t rowmask[kDecodeMaxSlots];  // tokens of each slot
+  int n_slots;
+  int last;  // a down item completes its column block
+  // a down item's (slot, token) pairs: pair j of the group's slot b is pbase[b] + j, and
+  // prow[pair] is its activation row (slot * 16 + token)
+  int pbase[kGroupSlots + 1];
+  int prow[kDecodeMaxPairs + kDecodeMaxT];
+  int lrow[kGroupSlots * 16];  // staged row of (slot b, token t) in this round, or -1
 };
 
-__host__ __device__ inline PlanPtrs plan_ptrs(void* plan) {
-  PlanPtrs p;
-  p.n_slots = (int32_t*)plan;
-  p.slot_expert = p.n_slots + 4;
-  p.coef = (float*)(p.slot_expert + ((kDecodeMaxSlots + 3) / 4) * 4);
-  return p;
+__device__ __forceinline__ int slot_of(const Plan& pl, int e) {
+  return pl.word_base[e >> 5] + __popc(pl.bits[e >> 5] & ((1u << (e & 31)) - 1u));
 }
 
-// ------------------------------------------------------------------------------- plan
-template <int MAXC>
-__global__ __launch_bounds__(1024) void decode_plan_kernel(
-    const float* __restrict__ L, const uint16_t* __restrict__ x, const float* __restrict__ R, int T,
-    int D, int E, int k, float tau, int has_shared, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_tok,
-    int32_t* __restrict__ slot_row, PlanPtrs plan) {
-  __shared__ int sel_e[kDecodeMaxT * kMaxTopK];
-  __shared__ float sel_w[kDecodeMaxT * kMaxTopK];
-  __shared__ uint32_t bits[32];      // touched experts, E <= 1024
-  __shared__ int word_base[33];
-  __shared__ int cnt[1024];
-  __shared__ int scan_tmp[1024];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < 32) bits[tid] = 0u;
-  cnt[tid] = 0;
-  __syncthreads();
-  if (wave < T) {
-    int e;
-    float w;
-    topk_token<MAXC>(L + (int64_t)wave * E, x + (int64_t)wave * D, R, D, E, k, tau, e, w);
-    if (lane < k) {
-      sel_e[wave * k + lane] = e;
-      sel_w[wave * k + lane] = w;
-      idx_out[wave * k + lane] = e;
-      w_out[wave * k + lane] = w;
-      atomicOr(&bits[e >> 5], 1u << (e & 31));
-      atomicAdd(&cnt[e], 1);
-    }
+// inclusive prefix sum over the first n lanes of a wavefront (n <= 64, power of two)
+__device__ __forceinline__ int wave_scan_incl(int v, int n) {
+  const int lane = threadIdx.x & 63;
+  for (int off = 1; off < n; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
   }
-  __syncthreads();
-  // distinct experts in ascending order: slot of e = set bits below it
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < 32; ++i) {
-      word_base[i] = acc;
-      acc += __popc(bits[i]);
-    }
-    word_base[32] = acc;
-    const int n = acc + (has_shared ? 1 : 0);
-    *plan.n_slots = n;
-    if (has_shared) plan.slot_expert[acc] = -1;
-  }
-  // exclusive scan of the per-expert counts (group offsets, as the grouped path's)
-  {
-    int v = tid < E ? cnt[tid] : 0;
-    scan_tmp[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int add = tid >= off ? scan_tmp[tid - off] : 0;
-      __syncthreads();
-      scan_tmp[tid] += add;
-      __syncthreads();
-    }
-    // scan_tmp[tid] is inclusive
-    if (tid < E) offsets[tid] = scan_tmp[tid] - v;
-    if (tid == 0) {
-      offsets[E] = T * k;
-      if (has_shared) offsets[E + 1] = T * k + T;
-    }
-  }
-  __syncthreads();
-  const int n_distinct = word_base[32];
-  const int n_slots = n_distinct + (has_shared ? 1 : 0);
-  // slot list and the combine weights (zero, then one entry per (token, slot) pair)
-  for (int e = tid; e < E; e += 1024)
-    if ((bits[e >> 5] >> (e & 31)) & 1u)
-      plan.slot_expert[word_base[e >> 5] + __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u))] = e;
-  for (int i = tid; i < n_slots * 16; i += 1024) {
-    const int s = i >> 4, t = i & 15;
-    plan.coef[i] = (has_shared && s == n_distinct && t < T) ? 1.f : 0.f;
-  }
-  __syncthreads();
-  if (tid < T * k) {
-    const int t = tid / k;
-    const int e = sel_e[tid];
-    const int slot = word_base[e >> 5] + __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u));
-    plan.coef[slot * 16 + t] = sel_w[tid];
-    // stable permuted row: the tokens before t that also picked e
-    int rank = 0;
-    for (int u = 0; u < t * k; ++u) rank += sel_e[u] == e ? 1 : 0;
-    const int row = scan_tmp[e] - cnt[e] + rank;
-    sorted_tok[row] = t;
-    slot_row[tid] = row;
-  }
-  if (has_shared && tid < T) sorted_tok[T * k + tid] = tid;
+  return v;
+}
+
+__device__ __forceinline__ int atomic_add_agent(int32_t* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// device-scope (coherent across the L2 caches) loads and stores
+__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4_t load_dev16(const void* p) {
+  const uint64_t lo = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi =
+      __hip_atomic_load((const uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
 }
 
 // ------------------------------------------------------------------------------- staging
@@ -168,70 +152,155 @@ __device__ __forceinline__ void stage(unsigned char* dst, int nch, Src src, int 
   }
 }
 
+// as stage(), with device-scope loads (data written by other workgroups of this launch)
+template <typename Src>
+__device__ __forceinline__ void stage_dev(unsigned char* dst, int nch, Src src, int wave, int nw,
+                                          int lane) {
+  const int n_ins = (nch + 63) >> 6;
+  for (int k = wave; k < n_ins; k += nw) {
+    int c = 64 * k + lane;
+    if (c >= nch) c = nch - 1;
+    __builtin_amdgcn_global_load_lds(src(c), dst + 1024 * k, 16, 0, 16 /* sc1: device scope */);
+  }
+}
+
 // the 8 bytes of words (w, w + 1) (w even) of staged code row r (cpr chunks per row)
 __device__ __forceinline__ u32x2_t lds_words(const unsigned char* rows, int r, int cpr, int w) {
   const int c = w >> 2;
   return *(const u32x2_t*)(rows + (r * cpr + (c ^ (r & chunk_mask(cpr)))) * 16 + (w & 3) * 4);
 }
 
+// ------------------------------------------------------------------------------- plan
+// Every workgroup: waves take tokens t, t + 8 (one wavefront selects one token's top k).
+// `writer` also stores the routing outputs: top-k ids and weights, group offsets (pairs
+// with a lower expert), permuted rows (stable: a pair's rank among the earlier pairs with
+// the same expert) and, with the shared expert, its T rows after the T k routed ones.
+template <int MAXC>
+__device__ void make_plan(const DecodeParams& p, Plan& pl, bool writer) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, E = p.E, k = p.k;
+  if (tid < 32) pl.bits[tid] = 0u;
+  for (int i = tid; i < kDecodeMaxSlots; i += kThreads) pl.rowmask[i] = 0u;
+  __syncthreads();
+  for (int t = wave; t < T; t += kWaves) {
+    int e;
+    float w;
+    topk_token<MAXC>(p.logits + (int64_t)t * E, p.x + (int64_t)t * p.D, p.R, p.D, E, k, p.tau, e, w);
+    if (lane < k) {
+      pl.sel_e[t * k + lane] = e;
+      pl.sel_w[t * k + lane] = w;
+      atomicOr(&pl.bits[e >> 5], 1u << (e & 31));
+      if (writer) {
+        p.idx[t * k + lane] = e;
+        p.w[t * k + lane] = w;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // slot of the first expert of each 32-expert word
+    const int c = lane < 32 ? __popc(pl.bits[lane]) : 0;
+    const int inc = wave_scan_incl(c, 32);
+    if (lane < 32) pl.word_base[lane] = inc - c;
+    if (lane == 31) {
+      pl.word_base[32] = inc;
+      pl.n_slots = inc + (p.has_shared ? 1 : 0);
+    }
+  }
+  __syncthreads();
+  const int n_distinct = pl.word_base[32], n_slots = pl.n_slots;
+  for (int e = tid; e < E; e += kThreads)
+    if ((pl.bits[e >> 5] >> (e & 31)) & 1u) pl.slot_exp[slot_of(pl, e)] = e;
+  if (p.has_shared && tid == 0) {
+    pl.slot_exp[n_distinct] = -1;
+    pl.rowmask[n_distinct] = (T < 32 ? (1u << T) : 0u) - 1u;
+  }
+  for (int i = tid; i < n_slots * 16; i += kThreads) {
+    const int s = i >> 4, t = i & 15;
+    pl.coef[i] = (p.has_shared && s == n_distinct && t < T) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  const int pairs = T * k;
+  if (tid < pairs) {
+    const int t = tid / k, e = pl.sel_e[tid], s = slot_of(pl, e);
+    pl.coef[s * 16 + t] = pl.sel_w[tid];
+    atomicOr(&pl.rowmask[s], 1u << t);
+    if (writer) {
+      int below = 0, rank = 0;
+      for (int u = 0; u < pairs; ++u) {
+        const int eu = pl.sel_e[u];
+        below += eu < e ? 1 : 0;
+        rank += (u < tid && eu == e) ? 1 : 0;
+      }
+      p.sorted_tok[below + rank] = t;
+      p.slot_row[tid] = below + rank;
+    }
+  }
+  if (writer) {
+    for (int e = tid; e <= E; e += kThreads) {
+      int below = 0;
+      for (int u = 0; u < pairs; ++u) below += pl.sel_e[u] < e ? 1 : 0;
+      p.offsets[e] = below;
+    }
+    if (p.has_shared) {
+      if (tid == 0) p.offsets[E + 1] = pairs + T;
+      if (tid < T) p.sorted_tok[pairs + tid] = tid;
+    }
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------------- gate_up
-// One workgroup of eight wavefronts per (slot, slice of 16 gate rows and the 16 matching up
-// rows).  The slice's codes (32 rows) and its scale and bias rows go to LDS first; while
-// they land, wavefront w loads its activations for the 256-K stages w, w + 8, ... from the
-// prepared x (rows past T read the zero row).  The eight partial sums meet through LDS (over
-// the code area, once every wavefront is done with it) in a fixed order; wavefront 0 applies
-// SwiGLU and stores the activations in the down kernel's fragment order:
-// act[slot][group][step][lane 16 q + row][8] = the eight values of prepared word
-// 8 group + 2 q + step of the row.
-constexpr int kUpWaves = 8;
-constexpr int kUpMaxD = 2048;
-constexpr int kUpCodeBytes = 32 * kUpMaxD / 2 + 1024;     // 32 rows of codes + slack
-constexpr int kUpSbBytes = 4 * 32 * (kUpMaxD / 64) + 1024;  // gate s, up s, gate b, up b
-static_assert(kUpCodeBytes >= (int)sizeof(f32x4_t) * kUpWaves * 2 * 64, "reduction area");
-__global__ __launch_bounds__(64 * kUpWaves) void decode_gate_up_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char codes[kUpCodeBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char sb[kUpSbBytes];
+// Item (slot s, slice sl): 16 gate rows 16 sl .. and the matching 16 up rows.  The slice's
+// codes (32 rows) and its scale and bias rows go to LDS first; while they land, wavefront
+// w loads the slot's token rows of the prepared x for the 256-K stages w, w + 8, ...
+// (other rows are zero).  The eight partial sums meet through LDS (over the code area, once
+// every wavefront is done with it) in a fixed order; wavefront 0 applies SwiGLU, stores the
+// slot's token rows (act[slot][token][F], columns in the prepared order of x, device-scope
+// stores) and, once they are complete, sets the item's done flag.
+__device__ void gate_up_item(const DecodeParams& p, const Plan& pl, unsigned char* area, int s,
+                             int sl) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = l & 15, q = l >> 4;
-  const int F = p.F, D = p.D, NSL = F / 16;
-  const int s = blockIdx.x / NSL, sl = blockIdx.x - s * NSL;
-  const PlanPtrs plan = plan_ptrs(p.plan);
-  const int n_slots = __builtin_amdgcn_readfirstlane(*plan.n_slots);
-  if (s >= n_slots) return;  // uniform, before any barrier
-  const int e = __builtin_amdgcn_readfirstlane(plan.slot_expert[s]);
+  const int F = p.F, D = p.D, KW = D >> 3, KG = D >> 6, CPR = D >> 5;
+  const int e = __builtin_amdgcn_readfirstlane(pl.slot_exp[s]);
   const Q4Ptrs& W = e >= 0 ? p.up_main : p.up_last;
-  const int KW = D >> 3, KG = D >> 6, CPR = D >> 5;
   const int64_t base_row = (int64_t)(e >= 0 ? e : 0) * (2 * F);
   const int64_t gate0 = base_row + 16 * sl, up0 = base_row + F + 16 * sl;
   const int mask = chunk_mask(CPR);
+  unsigned char* codes = area;
+  unsigned char* sb = area + kUpCodeBytes + kSlack;
   // staged rows 0..15: gate rows gate0 + r; 16..31: up rows up0 + r - 16
   stage(codes, 32 * CPR, [&](int c) {
     const int r = c / CPR, cs = c - r * CPR;
     const int64_t row = (r < 16 ? gate0 : up0 - 16) + r;
     return (const unsigned char*)(W.q + row * KW) + 16 * (cs ^ (r & mask));
-  }, wave, kUpWaves, l);
+  }, wave, kWaves, l);
   // four regions of 16 rows x KG bf16 (2 KG chunks each): gate s, up s, gate b, up b
   const int rch = 2 * KG;
   stage(sb, 4 * rch, [&](int c) {
     const int rg = c / rch, w = c - rg * rch;
     const uint16_t* base = (rg < 2 ? W.s : W.b) + ((rg & 1) ? up0 : gate0) * KG;
     return (const unsigned char*)base + 16 * w;
-  }, (wave + 4) % kUpWaves, kUpWaves, l);
-  // this wavefront's activations
-  const uint16_t* xr = p.xprep + (int64_t)(m < p.T ? m : p.T) * D + 16 * q;  // row T is zero
+  }, (wave + 4) % kWaves, kWaves, l);
+  // this wavefront's activations: the slot's token rows only
+  const uint32_t rows = pl.rowmask[s];
+  const bool mine = (rows >> m) & 1u;
+  const uint16_t* xr = p.xprep + (int64_t)m * D + 16 * q;
   const int NST = D >> 8;
-  constexpr int kMaxSt = kUpMaxD / 256 / kUpWaves;
+  constexpr int kMaxSt = kUpMaxD / 256 / kWaves;
   u32x4_t a[kMaxSt][4][2];
 #pragma unroll
   for (int v = 0; v < kMaxSt; ++v) {
-    const int st = wave + kUpWaves * v;
-    if (st < NST) {
+    const int st = wave + kWaves * v;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) a[v][g][h] = *(const u32x4_t*)(xr + 256 * st + 64 * g + 8 * h);
-    }
+      for (int h = 0; h < 2; ++h) {
+        a[v][g][h] = u32x4_t{0u, 0u, 0u, 0u};
+        if (st < NST && mine) a[v][g][h] = *(const u32x4_t*)(xr + 256 * st + 64 * g + 8 * h);
+      }
   }
   wait_vmcnt0();
   __syncthreads();
@@ -241,7 +310,7 @@ __global__ __launch_bounds__(64 * kUpWaves) void decode_gate_up_kernel(DecodePar
   f32x4_t acc[2] = {zero, zero};
 #pragma unroll
   for (int v = 0; v < kMaxSt; ++v) {
-    const int st = wave + kUpWaves * v;
+    const int st = wave + kWaves * v;
     if (st < NST) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -262,14 +331,14 @@ __global__ __launch_bounds__(64 * kUpWaves) void decode_gate_up_kernel(DecodePar
     }
   }
   __syncthreads();  // every wavefront is past its code reads
-  f32x4_t* part = (f32x4_t*)codes;  // [wave][2][64]
+  f32x4_t* part = (f32x4_t*)area;  // [wave][2][64]
   part[(wave * 2 + 0) * 64 + l] = acc[0];
   part[(wave * 2 + 1) * 64 + l] = acc[1];
   __syncthreads();
   if (wave == 0) {
     f32x4_t g4 = part[l], u4 = part[64 + l];
 #pragma unroll
-    for (int w = 1; w < kUpWaves; ++w) {
+    for (int w = 1; w < kWaves; ++w) {
       const f32x4_t gp = part[(2 * w) * 64 + l], up = part[(2 * w + 1) * 64 + l];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -278,129 +347,210 @@ __global__ __launch_bounds__(64 * kUpWaves) void decode_gate_up_kernel(DecodePar
       }
     }
     // natural column c = 16 sl + m: prepared word w = c / 8, position perm8(c % 8); word w
-    // is group w / 8, quarter (w % 8) / 2, step (w % 8) & 1 of the down kernel's fragments
-    const int c = 16 * sl + m, w = c >> 3, pos = perm8(c & 7);
-    const int g2 = w >> 3, qq = (w & 7) >> 1, hh = w & 1;
-    uint16_t* dst = p.act + ((((int64_t)s * (F >> 6) + g2) * 2 + hh) * 64 + 16 * qq) * 8 + pos;
+    // is group w / 8, quarter (w % 8) / 2, step (w % 8) & 1 of the down step's fragments
+    // natural column c = 16 sl + m sits at 8 (c / 8) + perm8(c % 8) of the prepared row.
+    // Lanes m and m + 4 (m % 8 < 4) hold columns c and c + 4, positions 2 j and 2 j + 1:
+    // the first stores both as one 32-bit word.
+    const int c = 16 * sl + m;
+    uint16_t* dst = p.act + (int64_t)s * 16 * F + 8 * (c >> 3) + perm8(c & 7);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
       const float gte = g4[i];
-      dst[(4 * q + i) * 8] = to_bf16(gte / (1.f + __expf(-gte)) * u4[i]);
+      const uint32_t v = to_bf16(gte / (1.f + __expf(-gte)) * u4[i]);
+      const uint32_t hi = (uint32_t)__shfl_down((int)v, 4, 64);
+      if ((m & 4) == 0 && ((rows >> r) & 1u)) store_dev((uint32_t*)(dst + (int64_t)r * F), v | (hi << 16));
     }
+    wait_vmcnt0();
+    if (l == 0) store_dev((uint32_t*)(p.sync + sync_flags_base(p.n_cb) + s * (F >> 4) + sl), 1u);
   }
 }
 
 // ------------------------------------------------------------------------------- down
-// One workgroup of eight wavefronts per 16 output columns.  The slots' experts and combine
-// weights go to LDS first; then, batch by batch of up to 12288 / F slots, the batch's
-// 16-row code slices and scale and bias rows go to LDS, and the (slot, 256-K part) units
-// are dealt to the wavefronts in turn: each unit loads its activation fragments (1 KB
-// contiguous each) and adds coef[slot][t] (s P' + (b - 128 s) X) over its four groups to
-// the wavefront's sums for its 16 columns and 16 token rows.  The eight partial sums meet
-// through LDS in a fixed order, then one bf16 row piece per token goes out.
-constexpr int kDownWaves = 8;
-constexpr int kDownMaxF = 1024;
-constexpr int kDownCodeArea = 96 * 1024;              // code slices of one batch
-constexpr int kDownSbArea = kDownCodeArea / 8;        // their scales and biases
-constexpr int kDownUnits = 4;                         // units' loads in flight per wavefront
-__global__ __launch_bounds__(64 * kDownWaves) void decode_down_combine_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char codes[kDownCodeArea + 1024];
-  __shared__ __attribute__((aligned(16))) unsigned char sbl[kDownSbArea + 1024];
-  __shared__ float red[kDownWaves][16][17];
-  __shared__ float scoef[kDecodeMaxSlots * 16];
-  __shared__ int sexp[kDecodeMaxSlots];
+// Item (column block cb, slot group sg): 16 output columns n0 = 16 cb .. against the slots
+// [s_lo, s_hi) of the group.  The slices' codes and scale and bias rows go to LDS first;
+// meanwhile wavefront 0 reads the done flags of the group's gate_up items (all lanes at
+// once) until every one is set.  Then, round by round, the group's (slot, token) rows of
+// activations go to LDS (device-scope loads, only the rows the tokens routed), and the
+// (slot, 256-K part) units are dealt to the wavefronts: a unit reads its A fragments from
+// the staged rows (zero for tokens not in the round) and adds coef[slot][t] (s P' +
+// (b - 128 s) X) over its four groups to the wavefront's sums for its 16 columns and 16
+// token rows.  The eight partial sums meet through LDS in a fixed order.  One group: the
+// bf16 row pieces go straight out.  Several: the group's sums go to `part`, and the last
+// group to arrive (counter per column block) adds all groups' sums in group order and
+// writes the output.
+__device__ void down_item(const DecodeParams& p, Plan& pl, unsigned char* area, int cb, int sg,
+                          int n_sg) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = l & 15, q = l >> 4;
-  const int F = p.F, D = p.D, n0 = 16 * blockIdx.x;
-  const int KW = F >> 3, KG = F >> 6, CPR = F >> 5;
-  const PlanPtrs plan = plan_ptrs(p.plan);
-  const int n_slots = __builtin_amdgcn_readfirstlane(*plan.n_slots);
-  for (int i = tid; i < n_slots * 16; i += 64 * kDownWaves) scoef[i] = plan.coef[i];
-  for (int i = tid; i < n_slots; i += 64 * kDownWaves) sexp[i] = plan.slot_expert[i];
-  __syncthreads();
-  const int NP = (KG + 3) >> 2;  // 256-K parts
-  const int per_batch = kDownCodeArea / (8 * F);  // 16 rows x F / 2 bytes per slot
+  const int F = p.F, D = p.D, n0 = 16 * cb;
+  const int KW = F >> 3, KG = F >> 6, CPR = F >> 5, NSL = F >> 4;
+  const int n_slots = pl.n_slots;
+  const int s_lo = sg * n_slots / n_sg, s_hi = (sg + 1) * n_slots / n_sg, nb = s_hi - s_lo;
   const int mask = chunk_mask(CPR);
+  unsigned char* codes = area;
+  unsigned char* sbl = area + kDownCodeArea + kSlack;
+  // activation area: one zero row (tokens a slot does not have read it), then the rows of
+  // a round
+  unsigned char* acts = sbl + kDownSbArea + kSlack;
+  unsigned char* arows = acts + 2 * F;
+  for (int i = tid; i < F / 8; i += kThreads) *(u32x4_t*)(acts + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
+  // codes: staged row r = 16 b + i is row n0 + i of slot s_lo + b's expert
+  stage(codes, nb * 16 * CPR, [&](int c) {
+    const int r = c / CPR, cs = c - r * CPR;
+    const int e = pl.slot_exp[s_lo + (r >> 4)];
+    const Q4Ptrs& W = e >= 0 ? p.down_main : p.down_last;
+    const int64_t row = (int64_t)(e >= 0 ? e : 0) * D + n0 + (r & 15);
+    return (const unsigned char*)(W.q + row * KW) + 16 * (cs ^ (r & mask));
+  }, wave, kWaves, l);
+  // scales then biases of each slot's 16 rows (16 KG bf16, 2 KG chunks each)
+  const int rch = 2 * KG;
+  stage(sbl, nb * 2 * rch, [&](int c) {
+    const int rg = c / rch, w = c - rg * rch;
+    const int e = pl.slot_exp[s_lo + (rg >> 1)];
+    const Q4Ptrs& W = e >= 0 ? p.down_main : p.down_last;
+    const int64_t row = (int64_t)(e >= 0 ? e : 0) * D + n0;
+    return (const unsigned char*)(((rg & 1) ? W.b : W.s) + row * KG) + 16 * w;
+  }, (wave + 4) % kWaves, kWaves, l);
+  if (wave == 0) {
+    // the group's pairs: slot b's first at pbase[b]
+    const int c = l < nb ? __popc(pl.rowmask[s_lo + l]) : 0;
+    const int inc = wave_scan_incl(c, 16);  // nb <= kGroupSlots <= 16
+    if (l < nb) pl.pbase[l] = inc - c;
+    if (l == nb - 1) pl.pbase[nb] = inc;
+    // the done flags of the group's gate_up items
+    const int32_t* fl = p.sync + sync_flags_base(p.n_cb) + s_lo * NSL;
+    const int nf = nb * NSL;
+    int spins = 0;
+    for (;;) {
+      int ok = 1;
+      for (int i = l; i < nf; i += 64) ok &= load_dev((const uint32_t*)(fl + i)) != 0u ? 1 : 0;
+      if (__all(ok)) break;
+      if (++spins > kSpinLimit) {
+        if (l == 0) atomic_add_agent(p.sync, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  wait_vmcnt0();
+  __syncthreads();
+  if (tid < nb) {
+    uint32_t mk = pl.rowmask[s_lo + tid];
+    int j = pl.pbase[tid];
+    while (mk) {
+      pl.prow[j++] = (s_lo + tid) * 16 + __builtin_ctz(mk);
+      mk &= mk - 1u;
+    }
+  }
+  __syncthreads();
+  const int npairs = pl.pbase[nb];
+  const int R = kDownActArea / (2 * F) - 1;  // activation rows per round
+  const int CPA = F >> 3;                 // 16-byte chunks per activation row
   const uint32_t magic = opaque_magic();
   const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   f32x4_t out = zero;
-  for (int s0 = 0; s0 < n_slots; s0 += per_batch) {
-    const int nb = n_slots - s0 < per_batch ? n_slots - s0 : per_batch;
-    if (s0 > 0) __syncthreads();  // the previous batch's LDS reads are done
-    // codes: staged row r = 16 b + i is row n0 + i of slot s0 + b's expert
-    stage(codes, nb * 16 * CPR, [&](int c) {
-      const int r = c / CPR, cs = c - r * CPR, b = r >> 4;
-      const int e = sexp[s0 + b];
-      const Q4Ptrs& W = e >= 0 ? p.down_main : p.down_last;
-      const int64_t row = (int64_t)(e >= 0 ? e : 0) * D + n0 + (r & 15);
-      return (const unsigned char*)(W.q + row * KW) + 16 * (cs ^ (r & mask));
-    }, wave, kDownWaves, l);
-    // scales then biases of each slot's 16 rows (16 KG bf16, 2 KG chunks each)
-    const int rch = 2 * KG;
-    stage(sbl, nb * 2 * rch, [&](int c) {
-      const int rg = c / rch, w = c - rg * rch, b = rg >> 1;
-      const int e = sexp[s0 + b];
-      const Q4Ptrs& W = e >= 0 ? p.down_main : p.down_last;
-      const int64_t row = (int64_t)(e >= 0 ? e : 0) * D + n0;
-      return (const unsigned char*)(((rg & 1) ? W.b : W.s) + row * KG) + 16 * w;
-    }, (wave + 4) % kDownWaves, kDownWaves, l);
+  for (int r0 = 0; r0 < npairs; r0 += R) {
+    const int nr = npairs - r0 < R ? npairs - r0 : R;
+    if (r0 > 0) __syncthreads();  // the previous round's reads are done
+    stage_dev(arows, nr * CPA, [&](int c) {
+      const int pr = c / CPA, w = c - pr * CPA;
+      return (const unsigned char*)(p.act + (int64_t)pl.prow[r0 + pr] * F) + 16 * w;
+    }, wave, kWaves, l);
+    if (tid < nb * 16) {
+      const int b = tid >> 4, t = tid & 15;
+      const uint32_t mk = pl.rowmask[s_lo + b];
+      const int pr = pl.pbase[b] + __popc(mk & ((1u << t) - 1u)) - r0;
+      pl.lrow[tid] = ((mk >> t) & 1u) && pr >= 0 && pr < nr ? pr : -1;
+    }
     wait_vmcnt0();
     __syncthreads();
-    const int units = nb * NP;
-    for (int u0 = wave; u0 < units; u0 += kDownWaves * kDownUnits) {
-      u32x4_t a[kDownUnits][4][2];
+    // Wavefront w: the 64-wide groups w, w + 8, ... of every slot, two slots per step as
+    // straight-line code (a step past the last slot repeats it with a zero weight).  Per
+    // slot b the LDS addresses move by fixed strides: code rows 16 b .. (same chunk order,
+    // as the row's swizzle depends on the row modulo 16), scale and bias rows, weights.
+    for (int g = wave; g < KG; g += kWaves) {
+      const unsigned char* c0 = codes + (m * CPR + ((2 * g + (q >> 1)) ^ (m & mask))) * 16 + 8 * (q & 1);
+      const unsigned char* s0 = sbl + (m * KG + g) * 2;
+      const unsigned char* a0p = arows + 128 * g + 32 * q;
+      auto slot = [&](int b, float wmul, f32x4_t& acc) __attribute__((always_inline)) {
+        const unsigned char* ar = a0p + pl.lrow[b * 16 + m] * (2 * F);  // -1: the zero row
+        const u32x4_t x0 = *(const u32x4_t*)ar;
+        const u32x4_t x1 = *(const u32x4_t*)(ar + 16);
+        const u32x2_t wd = *(const u32x2_t*)(c0 + b * 256 * CPR);
+        const float sg = bf16lo_to_f32(*(const uint16_t*)(s0 + b * 64 * KG));
+        const float bg = bf16lo_to_f32(*(const uint16_t*)(s0 + b * 64 * KG + 32 * KG));
+        const f32x4_t cf = *(const f32x4_t*)&pl.coef[(s_lo + b) * 16 + 4 * q];
+        const f32x4_t X = mfma16x16x32(x1, ones, mfma16x16x32(x0, ones, zero));
+        const f32x4_t P = mfma16x16x32(x1, unpack_word(wd[1], magic),
+                                       mfma16x16x32(x0, unpack_word(wd[0], magic), zero));
+        const float ws = wmul * sg, wc = wmul * fmaf(-128.f, sg, bg);
 #pragma unroll
-      for (int k = 0; k < kDownUnits; ++k) {
-        const int u = min(u0 + kDownWaves * k, units - 1);  // past the end: valid, not added
-        const int b = u / NP, pt = u - b * NP;
-        const uint16_t* af = p.act + (int64_t)(s0 + b) * KG * 2 * 512 + 8 * l;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int g = min(4 * pt + g4, KG - 1);  // past K: a valid group, not added
-#pragma unroll
-          for (int h = 0; h < 2; ++h) a[k][g4][h] = *(const u32x4_t*)(af + (2 * g + h) * 512);
-        }
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(cf[i], fmaf(ws, P[i], wc * X[i]), acc[i]);
+      };
+      f32x4_t out2 = zero;
+      for (int b = 0; b < nb; b += 2) {
+        const bool two = b + 1 < nb;
+        slot(b, 1.f, out);
+        slot(two ? b + 1 : b, two ? 1.f : 0.f, out2);
       }
 #pragma unroll
-      for (int k = 0; k < kDownUnits; ++k) {
-        const int u = u0 + kDownWaves * k;
-        if (u < units) {
-          const int b = u / NP, pt = u - b * NP;
-          f32x4_t y = zero;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int g = 4 * pt + g4;
-            if (g < KG) {
-              const u32x2_t wd = lds_words(codes, 16 * b + m, CPR, 8 * g + 2 * q);
-              const f32x4_t X = mfma16x16x32(a[k][g4][1], ones, mfma16x16x32(a[k][g4][0], ones, zero));
-              const f32x4_t P = mfma16x16x32(a[k][g4][1], unpack_word(wd[1], magic),
-                                             mfma16x16x32(a[k][g4][0], unpack_word(wd[0], magic), zero));
-              const int so = ((2 * b) * 16 * KG + m * KG + g) * 2;
-              const float sg = bf16lo_to_f32(*(const uint16_t*)(sbl + so));
-              const float bg = bf16lo_to_f32(*(const uint16_t*)(sbl + so + 32 * KG));
-              const float cg = fmaf(-128.f, sg, bg);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) y[i] = fmaf(sg, P[i], fmaf(cg, X[i], y[i]));
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[i] = fmaf(scoef[(s0 + b) * 16 + 4 * q + i], y[i], out[i]);
-        }
-      }
+      for (int i = 0; i < 4; ++i) out[i] += out2[i];
     }
   }
-  // out holds rows 4 q + i, column m
+  __syncthreads();  // every wavefront is past its LDS reads
+  float* red = (float*)area;  // [wave][16][17]: out holds rows 4 q + i, column m
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * q + i][m] = out[i];
+  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * q + i) * 17 + m] = out[i];
   __syncthreads();
+  const int t = tid >> 4, c = tid & 15;
+  float v = 0.f;
   if (tid < 256) {
-    const int t = tid >> 4, c = tid & 15;
-    float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDownWaves; ++w) v += red[w][t][c];
-    if (t < p.T) p.out[(int64_t)t * D + n0 + c] = to_bf16(v);
+    for (int w = 0; w < kWaves; ++w) v += red[(w * 16 + t) * 17 + c];
+  }
+  if (n_sg == 1) {
+    if (tid < 256 && t < p.T) p.out[(int64_t)t * D + n0 + c] = to_bf16(v);
+    return;
+  }
+  float* part = p.part + (int64_t)cb * 256;
+  const int64_t gstride = (int64_t)p.n_cb * 256;
+  if (tid < 256 && t < p.T) store_dev((uint32_t*)(part + sg * gstride + tid), __float_as_uint(v));
+  wait_vmcnt0();
+  __syncthreads();
+  if (tid == 0) pl.last = atomic_add_agent(p.sync + kSyncCb + 32 * cb, 1) == n_sg - 1;
+  __syncthreads();
+  if (pl.last) {
+    if (tid < 256 && t < p.T) {
+      float sum = 0.f;
+      for (int g = 0; g < n_sg; ++g)
+        sum += __uint_as_float(load_dev((const uint32_t*)(part + g * gstride + tid)));
+      p.out[(int64_t)t * D + n0 + c] = to_bf16(sum);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------- launch
+// Two workgroups per compute unit (LDS and, for E <= 256, 128 registers per lane); the
+// 1024-expert selection needs more registers and runs one per compute unit.
+template <int MAXC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXC <= 4 ? 4 : 1)))
+void decode_layer_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) Plan pl;
+  __shared__ __attribute__((aligned(16))) unsigned char area[kArea];
+  make_plan<MAXC>(p, pl, blockIdx.x == 0);
+  const int n_slots = pl.n_slots, NSL = p.F >> 4;
+  const int n_up = n_slots * NSL;
+  const int n_sg = (n_slots + p.group_slots - 1) / p.group_slots;
+  const int t = blockIdx.x;
+  if (t < n_up) {
+    gate_up_item(p, pl, area, t / NSL, t - (t / NSL) * NSL);
+  } else if (t < n_up + p.n_cb * n_sg) {
+    const int d = t - n_up, sg = d / p.n_cb;
+    down_item(p, pl, area, d - sg * p.n_cb, sg, n_sg);
   }
 }
 
@@ -408,37 +558,36 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_combine_kernel(De
 
 bool decode_supported(int T, int D, int E, int k, int F) {
   return T >= 1 && T <= kDecodeMaxT && T * k <= kDecodeMaxPairs && E <= 1024 && D % 256 == 0 &&
-         D <= kUpMaxD && F % 64 == 0 && F <= kDownMaxF;
+         D <= kUpMaxD && F % 64 == 0 && F <= kMaxF;
 }
 
-size_t decode_plan_bytes() {
-  return 16 + ((kDecodeMaxSlots + 3) / 4) * 16 + (size_t)kDecodeMaxSlots * 16 * 4;
+int decode_group_slots(int F) {
+  const int by_area = kDownSbArea / F;  // nb F bytes of scales and biases, 8 nb F of codes
+  return by_area < kGroupSlots ? by_area : kGroupSlots;
 }
 
-void launch_decode_plan(const float* L, const uint16_t* x, const float* R, int T, int D, int E,
-                        int k, float tau, bool has_shared, int32_t* idx, float* w,
-                        int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, void* plan,
-                        hipStream_t s) {
-  const PlanPtrs pp = plan_ptrs(plan);
-  const dim3 grid(1), block(1024);
-  if (E <= 64)
-    hipLaunchKernelGGL(decode_plan_kernel<1>, grid, block, 0, s, L, x, R, T, D, E, k, tau,
-                       has_shared ? 1 : 0, idx, w, offsets, sorted_tok, slot_row, pp);
-  else if (E <= 256)
-    hipLaunchKernelGGL(decode_plan_kernel<4>, grid, block, 0, s, L, x, R, T, D, E, k, tau,
-                       has_shared ? 1 : 0, idx, w, offsets, sorted_tok, slot_row, pp);
+int decode_sync_ints(int D, int F, int max_slots) {
+  return sync_flags_base(D / 16) + max_slots * (F / 16);
+}
+
+size_t decode_part_bytes(int D, int F, int max_slots) {
+  const int gs = decode_group_slots(F);
+  return (size_t)((max_slots + gs - 1) / gs) * (D / 16) * 256 * sizeof(float);
+}
+
+size_t decode_act_bytes(int F, int max_slots) { return (size_t)max_slots * 16 * F * 2; }
+
+void launch_decode_layer(const DecodeParams& p, int max_slots, hipStream_t s) {
+  // the most items any routing can give; workgroups past the actual count return
+  const int gs = decode_group_slots(p.F);
+  const int64_t items = (int64_t)max_slots * (p.F / 16) + (int64_t)p.n_cb * ((max_slots + gs - 1) / gs);
+  const dim3 grid((unsigned)items), block(kThreads);
+  if (p.E <= 64)
+    hipLaunchKernelGGL(decode_layer_kernel<1>, grid, block, 0, s, p);
+  else if (p.E <= 256)
+    hipLaunchKernelGGL(decode_layer_kernel<4>, grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(decode_plan_kernel<16>, grid, block, 0, s, L, x, R, T, D, E, k, tau,
-                       has_shared ? 1 : 0, idx, w, offsets, sorted_tok, slot_row, pp);
-}
-
-void launch_decode_gate_up(const DecodeParams& p, int max_slots, hipStream_t s) {
-  hipLaunchKernelGGL(decode_gate_up_kernel, dim3(max_slots * (p.F / 16)), dim3(64 * kUpWaves), 0,
-                     s, p);
-}
-
-void launch_decode_down_combine(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_down_combine_kernel, dim3(p.D / 16), dim3(64 * kDownWaves), 0, s, p);
+    hipLaunchKernelGGL(decode_layer_kernel<16>, grid, block, 0, s, p);
 }
 
 }  // namespace moeq4

@@ -19,6 +19,11 @@ void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T
 // xprep as above.  planes_ready: Rs already holds the planes of this R (the split is
 // skipped).
 bool router_uses_planes(int T, int D);
+// the one-wavefront-per-expert router (T <= 16, D % 256 == 0); its workgroups also clear
+// n_zero words at `zero` for the kernel that follows
+bool router_small_ok(int T, int D);
+void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
+                         uint16_t* xprep, int32_t* zero, int n_zero, hipStream_t s);
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
                    uint16_t* xprep, hipStream_t s, bool planes_ready = false);
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
@@ -161,28 +166,40 @@ bool wide_supported(int N, int K, bool swiglu, int a_rows);
 void launch_wide(WideParams p, bool swiglu, int64_t n_tiles_bound, int n_cu, hipStream_t s);
 
 // ---------------------------------------------------------------- decode-sized layer
-// T <= 16 tokens (decode.hip): plan (top-k, touched-expert slots, combine weights, routing
-// outputs), gate_up + SwiGLU per (slot, 16-row slice), down fused with the combine per 16
-// output columns.  No permuted rows, no expert-output array.
+// T <= 16 tokens (decode.hip): after the few-token router (which clears the counters),
+// one launch whose workgroups each compute the plan (top-k, touched-expert slots, combine
+// weights; workgroup 0 also the routing outputs) and then one item, in workgroup order:
+// gate_up + SwiGLU per (slot, 16-row slice), then down fused with the combine per (16
+// output columns, group of slots), each down item waiting on its slots' gate_up items.
 constexpr int kDecodeMaxT = 16;
 constexpr int kDecodeMaxPairs = 128;                  // T * k
 constexpr int kDecodeMaxSlots = kDecodeMaxPairs + 1;  // distinct experts + the shared one
 struct DecodeParams {
-  int32_t T, D, F;
+  int32_t T, D, E, k, F, has_shared;
+  int32_t group_slots;  // most slots per down item
+  int32_t n_cb;         // D / 16 output column blocks
+  float tau;            // top-k refinement gap
+  const float* logits;  // [T, E] fp32
+  const uint16_t* x;    // [T, D] bf16 (the exact top-k rescoring)
+  const float* R;       // [E, D] fp32
   const uint16_t* xprep;  // prepared x [T + 1, D], row T zero
-  void* plan;             // decode_plan_bytes() bytes
-  uint16_t* act;          // bf16 [max slots][16][F], prepared column order
-  uint16_t* out;          // bf16 [T, D]
+  int32_t* idx;         // [T, k] routing outputs (written by workgroup 0)
+  float* w;             // [T, k]
+  int32_t* offsets;     // [E + 2]
+  int32_t* sorted_tok;  // [T k + T]
+  int32_t* slot_row;    // [T k]
+  int32_t* sync;        // decode_sync_ints() counters and flags, zero at launch
+  float* part;          // down partial sums [groups][n_cb][16][16]
+  uint16_t* act;        // bf16 [max slots][16 tokens][F], prepared column order
+  uint16_t* out;        // bf16 [T, D]
   Q4Ptrs up_main, up_last, down_main, down_last;  // experts [E, ...]; the shared expert
 };
 bool decode_supported(int T, int D, int E, int k, int F);
-size_t decode_plan_bytes();
-void launch_decode_plan(const float* L, const uint16_t* x, const float* R, int T, int D, int E,
-                        int k, float tau, bool has_shared, int32_t* idx, float* w,
-                        int32_t* offsets, int32_t* sorted_tok, int32_t* slot_row, void* plan,
-                        hipStream_t s);
-void launch_decode_gate_up(const DecodeParams& p, int max_slots, hipStream_t s);
-void launch_decode_down_combine(const DecodeParams& p, hipStream_t s);
+int decode_group_slots(int F);
+int decode_sync_ints(int D, int F, int max_slots);
+size_t decode_part_bytes(int D, int F, int max_slots);
+size_t decode_act_bytes(int F, int max_slots);
+void launch_decode_layer(const DecodeParams& p, int max_slots, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 void launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* slot_row, const float* w,

@@ -464,17 +464,17 @@ __global__ __launch_bounds__(kF32Threads) void router_logits_f32_kernel(
 }
 
 constexpr int kSmallTok = 16;  // the one-wavefront-per-expert kernel serves T <= 16
-static void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
-                                uint16_t* xprep, hipStream_t s);
+
+bool router_small_ok(int T, int D) { return T <= kSmallTok && D % 256 == 0; }
 
 bool router_uses_planes(int T, int D) {
-  return !(T <= kSmallTok && D % 256 == 0) && !(T < 2048 && D % kF32KC == 0);
+  return !router_small_ok(T, D) && !(T < 2048 && D % kF32KC == 0);
 }
 
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
                    uint16_t* xprep, hipStream_t s, bool planes_ready) {
-  if (T <= kSmallTok && D % 256 == 0) {
-    launch_router_small(x, R, L, T, D, E, xprep, s);
+  if (router_small_ok(T, D)) {
+    launch_router_small(x, R, L, T, D, E, xprep, nullptr, 0, s);
     return;
   }
   if (T < 2048 && D % kF32KC == 0) {
@@ -542,13 +542,15 @@ void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D
 // tokens, T rounded up; rows past T re-read the last row and are dropped), all of a step
 // issued before any is used (and a few steps at a time); the lane sums in fp32 in k order, then the wavefront sums in
 // a fixed DPP order.  The workgroups also write the prepared copy of x (runs of 8 columns
-// in the order 0,4,1,5,2,6,3,7, one zero row after the last token).
+// in the order 0,4,1,5,2,6,3,7, one zero row after the last token), and clear n_zero words
+// at `zero` (the next kernel's counters and flags).
 template <int TT>
 __global__ __launch_bounds__(256) void router_logits_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ R, float* __restrict__ L, int T, int D,
-    int E, uint16_t* __restrict__ xprep) {
+    int E, uint16_t* __restrict__ xprep, int32_t* __restrict__ zero, int n_zero) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_zero; i += gridDim.x * 256) zero[i] = 0;
   if (xprep) {
     const int pieces = (T + 1) * (D >> 3);
     for (int pc = blockIdx.x * 256 + threadIdx.x; pc < pieces; pc += gridDim.x * 256) {
@@ -599,15 +601,18 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
   }
 }
 
-static void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
-                                uint16_t* xprep, hipStream_t s) {
+void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int D, int E,
+                         uint16_t* xprep, int32_t* zero, int n_zero, hipStream_t s) {
   const dim3 grid((E + 3) / 4), block(256);
   if (T <= 1)
-    hipLaunchKernelGGL(router_logits_small_kernel<1>, grid, block, 0, s, x, R, L, T, D, E, xprep);
+    hipLaunchKernelGGL(router_logits_small_kernel<1>, grid, block, 0, s, x, R, L, T, D, E, xprep,
+                       zero, n_zero);
   else if (T <= 4)
-    hipLaunchKernelGGL(router_logits_small_kernel<4>, grid, block, 0, s, x, R, L, T, D, E, xprep);
+    hipLaunchKernelGGL(router_logits_small_kernel<4>, grid, block, 0, s, x, R, L, T, D, E, xprep,
+                       zero, n_zero);
   else
-    hipLaunchKernelGGL(router_logits_small_kernel<16>, grid, block, 0, s, x, R, L, T, D, E, xprep);
+    hipLaunchKernelGGL(router_logits_small_kernel<16>, grid, block, 0, s, x, R, L, T, D, E, xprep,
+                       zero, n_zero);
 }
 
 }  // namespace moeq4

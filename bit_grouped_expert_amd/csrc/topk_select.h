@@ -61,6 +61,22 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   }));
 }
 
+// Butterfly reductions with the result in every lane, no scalar round trip: within each
+// row of 16 lanes (quad swaps, then rotations by 4 and 8), then across row pairs and
+// halves with the gfx950 lane swaps (each returns the two values a lane and its partner
+// hold; op takes both).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_all_reduce(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows r, r ^ 1
+  v = op((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves
+  return op((uint32_t)b[0], (uint32_t)b[1]);
+}
+
 // (value, expert) pair order: larger value first, then lower expert id.
 struct Cand {
   double v;
@@ -89,41 +105,57 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
     key[c] = e < E ? max(ordered_bits(val[c]), 1u) : 0u;
   }
 
-  // lane j keeps the j-th selection.  A round takes the largest logit of the wavefront
-  // (one 32-bit reduction); only when several lanes hold it does a second reduction pick
-  // the lowest expert id among them.  Within a lane the lower slot (lower id) wins ties.
+  // Each lane first sorts its own MAXC (key, slot) pairs, best first (larger key, then the
+  // lower slot, i.e. the lower expert id), with a fixed merge network.  Lane j keeps the
+  // j-th selection.  A round takes the largest head of the wavefront, then the lowest
+  // expert id among the lanes that hold it (two all-lane reductions); the winning lane
+  // drops its head.  No branch depends on lane data.
+  uint32_t sk[MAXC];
+  int sc[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    sk[c] = key[c];
+    sc[c] = c;
+  }
+  // Batcher's odd-even merge sort (MAXC a power of two): compare-exchange (i, i + d)
+#pragma unroll
+  for (int pw = 1; pw < MAXC; pw <<= 1)
+#pragma unroll
+    for (int d = pw; d >= 1; d >>= 1)
+#pragma unroll
+      for (int j0 = d % pw; j0 + d < MAXC; j0 += 2 * d)
+#pragma unroll
+        for (int i = 0; i < d; ++i) {
+          const int x = i + j0, y = i + j0 + d;
+          if (y < MAXC && x / (2 * pw) == y / (2 * pw)) {
+            const bool swap = sk[y] > sk[x] || (sk[y] == sk[x] && sc[y] < sc[x]);
+            const uint32_t kx = sk[x], ky = sk[y];
+            const int cx = sc[x], cy = sc[y];
+            sk[x] = swap ? ky : kx;
+            sk[y] = swap ? kx : ky;
+            sc[x] = swap ? cy : cx;
+            sc[y] = swap ? cx : cy;
+          }
+        }
   int my_e = -1;
   float my_v = 0.f;
   const int nsel = (k + 1 < E) ? k + 1 : E;
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
   for (int j = 0; j < nsel; ++j) {
-    uint32_t lb = key[0];
-    int lc = 0;
-#pragma unroll
-    for (int c = 1; c < MAXC; ++c)
-      if (key[c] > lb) {
-        lb = key[c];
-        lc = c;
-      }
-    const uint32_t hi = wave_max_u32(lb);
-    const uint64_t holders = __ballot(lb == hi);
-    int e;
-    if (__popcll(holders) == 1) {
-      const int wl = __builtin_ctzll(holders);
-      e = 64 * __builtin_amdgcn_readlane(lc, wl) + wl;
-    } else {
-      const uint32_t r = wave_max_u32(lb == hi ? 0xFFFFFFFFu - (uint32_t)(64 * lc + lane) : 0u);
-      e = (int)(0xFFFFFFFFu - r);
-    }
+    const uint32_t hk = sk[0];
+    const uint32_t hi = wave_all_reduce(hk, umax);
+    const int e = (int)wave_all_reduce(hk == hi ? (uint32_t)(64 * sc[0] + lane) : 0xFFFFFFFFu, umin);
     const float v = unordered_bits(hi);
-    if (lane == j) {
-      my_e = e;
-      my_v = v;
-    }
-    if ((e & 63) == lane) {
+    my_e = lane == j ? e : my_e;
+    my_v = lane == j ? v : my_v;
+    const bool pop = (e & 63) == lane;
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c)
-        if (c == (e >> 6)) key[c] = 0u;
+    for (int c = 0; c + 1 < MAXC; ++c) {
+      sk[c] = pop ? sk[c + 1] : sk[c];
+      sc[c] = pop ? sc[c + 1] : sc[c];
     }
+    sk[MAXC - 1] = pop ? 0u : sk[MAXC - 1];
   }
 
   // fp64 logits of up to four experts (uniform ids ce[0 .. nb-1]; slots past nb repeat

@@ -102,8 +102,10 @@ typedef enum {
   MOE_ENGINE_WIDE = 3,     /* K % 256 == 0, K <= 2048, N % 256 == 0: tiles of up to 128
                               rows (large groups) */
   MOE_ENGINE_DECODE = 4    /* moe_layer_forward_ex only: the decode-sized chain (T <= 16,
-                              T * k <= 128, d_model % 256 == 0; the automatic choice there):
-                              no permuted rows, the down product fused with the combine */
+                              T * k <= 128, E <= 1024, d_model % 256 == 0, d_model <= 2048,
+                              d_ff <= 1024; the automatic choice there): the router, then
+                              one persistent launch (plan, gate_up, down fused with the
+                              combine); no permuted rows */
 } moe_engine;
 
 /* Options of moe_layer_forward_ex.  A NULL options pointer equals all fields zero. */
