@@ -6,7 +6,9 @@ SwiGLU, grouped down, weighted combine) over one batch of synthetic tokens whose
 are resident in HBM.  The headline workload is the 512-token prefill of a
 Qwen3.6-35B-A3B-shaped layer (d_model 2048, 256 experts top-8 + 1 shared expert, d_ff 512,
 int4 weights with bf16 scale and bias per 64); the 8192-token prefill with Zipf-skewed
-routing is measured in the same run and reported in the same line (`zipf8192`).  Four
+routing is measured in the same run and reported in the same line (`zipf8192`), and so is the
+per-layer latency of the decode-sized layer at 1 and 4 tokens, eager and as graph replays
+(`decode`).  Four
 distinct weight sets (455 MB each; together more than the 256 MB Infinity Cache) rotate so
 that every step streams its weights from HBM.
 
@@ -20,7 +22,7 @@ from a separate pass after each timed region with an event at every stage bounda
 those events themselves cost a few microseconds per step.
 
     python bench.py [--steps K] [--warmup W] [--config prefill512|zipf8192|uniform8192|...]
-                    [--no-secondary] [--no-cpu-baseline] [--copy-probe]
+                    [--no-secondary] [--no-decode] [--no-cpu-baseline] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -70,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill512")
     ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-sized latency object (T=1 and T=4)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the 8192-token Zipf layer measured after the headline one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,6 +233,69 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     }, (x, router)
 
 
+def measure_decode(cfg, sets, torch, L, dev, wl, layers=200):
+    """Per-layer latency of the decode-sized layer (T <= 16): `layers` back-to-back layer calls
+    rotating the weight sets, issued eagerly and as replays of one captured graph of four
+    layers (one per weight set, so each layer's weights come from HBM).  The HBM floor is the
+    layer's algorithmic bytes (touched experts' codes, scales and biases, the router, x and
+    out) at the published 8 TB/s."""
+    x, router = wl.make_activations(cfg, 0)
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    ws = dev.workspace(shp)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
+    n = len(sets)
+
+    def layer(i, stream):
+        lw = sets[i % n]
+        L.moe_layer_forward(shp, xd, rd, lw.experts, lw.shared, out, ws, stream=stream)
+
+    cur = torch.cuda.current_stream()
+    for i in range(2 * n):
+        layer(i, cur)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(layers):
+        layer(i, cur)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / layers
+
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for i in range(n):
+            layer(i, side)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for i in range(n):
+            layer(i, cap)
+    for _ in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, layers // n)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / (reps * n)
+    del g
+
+    lay = L.moe_workspace_layout(shp)
+    offs = ws[lay.offsets:lay.offsets + 4 * (cfg.E + 2)].cpu().numpy().view(np.int32)
+    touched = int(np.count_nonzero(np.diff(offs[:cfg.E + 1]))) + 1
+    nbytes = float(wl.algorithmic_bytes(cfg, touched))
+    floor_us = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    log(f"bench: {cfg.name}: eager {eager_us:.1f} us/layer, graph replay {graph_us:.1f} us/layer, "
+        f"HBM floor {floor_us:.2f} us ({touched} experts touched)")
+    return {"T": cfg.T, "touched_groups": touched, "eager_us_per_layer": eager_us,
+            "graph_us_per_layer": graph_us, "algorithmic_bytes": nbytes,
+            "hbm_floor_us": floor_us, "floor_frac_graph": floor_us / graph_us,
+            "layers_timed": layers}
+
+
 def hbm_ceiling(torch, dev):
     """Measured streaming ceiling: a plain device copy of 1 GiB (2 GiB moved) and a streaming
     read of 2 GiB (torch's sum), best of five each, timed with fence-free HIP events."""
@@ -360,6 +427,15 @@ def main():
                                  "same shape and weights",
                      "steps": args.steps, "warmup": min(args.warmup, 20), **s_res}
 
+    decode = None
+    if not args.no_decode:
+        decode = {"workload": "decode-sized layers (T=1 and T=4 tokens), same shape and weights: "
+                              "the router, then one launch (plan, gate_up, down + combine)"}
+        for name in ("decode1", "decode4"):
+            dcfg = wl.CONFIGS[name]
+            if (dcfg.D, dcfg.E, dcfg.F, dcfg.bias) == (cfg.D, cfg.E, cfg.F, cfg.bias):
+                decode[name] = measure_decode(dcfg, sets, torch, L, dev, wl)
+
     ceiling = hbm_ceiling(torch, dev)
     log(f"bench: HBM ceiling copy {ceiling['copy_gbs']:.0f} GB/s, read {ceiling['read_gbs']:.0f} GB/s")
     main_res["roofline"]["frac_of_measured_ceiling"] = (
@@ -399,6 +475,7 @@ def main():
         "roofline": main_res["roofline"],
         "layer_roofline": main_res["layer_roofline"],
         "zipf8192": secondary,
+        "decode": decode,
         "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
