@@ -8,7 +8,7 @@ Qwen3.6-35B-A3B-shaped layer (d_model 2048, 256 experts top-8 + 1 shared expert,
 int4 weights with bf16 scale and bias per 64); the 8192-token prefill with Zipf-skewed
 routing is measured in the same run and reported in the same line (`zipf8192`), and so is the
 per-layer latency of the decode-sized layer at 1 and 4 tokens, eager and as graph replays
-(`decode`).  Four
+(`decode`), and the 32768-token layer as one call and in bounded chunks (`long32768`).  Four
 distinct weight sets (455 MB each; together more than the 256 MB Infinity Cache) rotate so
 that every step streams its weights from HBM.
 
@@ -22,7 +22,7 @@ from a separate pass after each timed region with an event at every stage bounda
 those events themselves cost a few microseconds per step.
 
     python bench.py [--steps K] [--warmup W] [--config prefill512|zipf8192|uniform8192|...]
-                    [--no-secondary] [--no-decode] [--no-cpu-baseline] [--copy-probe]
+                    [--no-secondary] [--no-decode] [--no-long] [--no-cpu-baseline] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill512")
     ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 32768-token layer (single call vs bounded chunks)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-sized latency object (T=1 and T=4)")
     ap.add_argument("--no-secondary", action="store_true",
@@ -296,6 +298,41 @@ def measure_decode(cfg, sets, torch, L, dev, wl, layers=200):
             "layers_timed": layers}
 
 
+def measure_long(cfg, sets, torch, L, dev, wl, chunks=(8192, 16384), reps=3):
+    """The long-prompt layer (T = 32768) as one call and as moe_layer_forward_chunked in chunks
+    of each size in `chunks` tokens with a workspace of one chunk: per-layer time over `reps`
+    passes of the four weight sets, and the workspace sizes."""
+    x, router = wl.make_activations(cfg, 0)
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
+    res = {"T": cfg.T}
+    for mode in ["single"] + [f"chunked_{c}" for c in chunks]:
+        if mode == "single":
+            nb = L.moe_workspace_bytes(shp)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            call = lambda lw: L.moe_layer_forward(shp, xd, rd, lw.experts, lw.shared, out, ws)
+        else:
+            chunk = int(mode.split("_")[1])
+            nb = L.moe_chunked_workspace_bytes(shp, chunk)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            call = lambda lw, chunk=chunk, ws=ws: L.moe_layer_forward_chunked(
+                shp, xd, rd, lw.experts, lw.shared, out, chunk, ws)
+        for lw in sets:
+            call(lw)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for lw in sets:
+                call(lw)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * len(sets))
+        res[mode] = {"ms_per_layer": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "workspace_bytes": nb}
+        log(f"bench: {cfg.name} {mode}: {ms:.3f} ms/layer, workspace {nb / 1e6:.1f} MB")
+        del ws
+    return res
+
+
 def hbm_ceiling(torch, dev):
     """Measured streaming ceiling: a plain device copy of 1 GiB (2 GiB moved) and a streaming
     read of 2 GiB (torch's sum), best of five each, timed with fence-free HIP events."""
@@ -436,6 +473,13 @@ def main():
             if (dcfg.D, dcfg.E, dcfg.F, dcfg.bias) == (cfg.D, cfg.E, cfg.F, cfg.bias):
                 decode[name] = measure_decode(dcfg, sets, torch, L, dev, wl)
 
+    long = None
+    lcfg = wl.CONFIGS["long32768"]
+    if not args.no_long and (lcfg.D, lcfg.E, lcfg.F, lcfg.bias) == (cfg.D, cfg.E, cfg.F, cfg.bias):
+        long = {"workload": "long32768: one MoE layer at T=32768 per weight set, same shape and "
+                            "weights, single call vs bounded chunks",
+                **measure_long(lcfg, sets, torch, L, dev, wl)}
+
     ceiling = hbm_ceiling(torch, dev)
     log(f"bench: HBM ceiling copy {ceiling['copy_gbs']:.0f} GB/s, read {ceiling['read_gbs']:.0f} GB/s")
     main_res["roofline"]["frac_of_measured_ceiling"] = (
@@ -476,6 +520,7 @@ def main():
         "layer_roofline": main_res["layer_roofline"],
         "zipf8192": secondary,
         "decode": decode,
+        "long32768": long,
         "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
     }

@@ -16,10 +16,12 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr float kRefineGap = 1e-4f;
-// average rows per group from which the wide-tile engine is the automatic choice
-// (measured: at 8192 tokens, about 290 rows per group, 955 against 964 us for both GEMMs;
-// at 32768, 3.06 against 3.29 ms)
-constexpr int64_t kWideMinAvgRows = 192;
+// average rows per group from which the wide-tile engine is the automatic choice.
+// Measured on the layer's gate_up shape (N 1024, K 2048, 257 groups) with the same row
+// count in every group: resident tiles are faster up to 32 rows per group (32: 118 against
+// 149 us), wide tiles from 48 on (48: 170 against 194 us; 64: 188 against 211; 128: 284
+// against 429).
+constexpr int64_t kWideMinAvgRows = 40;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
