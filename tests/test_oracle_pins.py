@@ -339,3 +339,84 @@ def test_zipf_routing_skew():
     cnt = oracle.expert_histogram(idx, cfg.E)
     assert np.all(cnt[-wl.ZIPF_MASKED:] == 0)
     assert cnt[0] > 4 * np.median(cnt)
+
+
+# ----------------------------------------------------------------------------- decode attention
+# MarkTechPost, same page, body paragraph 4 (grouped-query attention, 16 query heads and two
+# KV heads) and paragraph 8 (decode over the KV cache).  bf16 bit patterns are written by hand
+# here (exact small values), not through the library's generators.
+def _bf(vals):
+    """Exact bf16 bit patterns of float32 values that bf16 holds exactly."""
+    a = np.asarray(vals, dtype=np.float32)
+    u = a.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "values must be exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def test_attention_single_position_returns_its_value_row():
+    """ctx = 1: softmax over one score is 1, so every head returns its KV head's value row; this
+    also pins the head mapping h -> h // (n_q / n_kv)."""
+    rng = np.random.default_rng(0)
+    n_q, n_kv, d = 16, 2, 128
+    q = _bf(rng.integers(-4, 5, (n_q, d)).astype(np.float32))
+    k = _bf(rng.integers(-4, 5, (n_kv, 3, d)).astype(np.float32))
+    v = _bf(rng.integers(-8, 9, (n_kv, 3, d)).astype(np.float32))
+    out = oracle.gqa_decode_attention(q, k, v, 1)
+    vf = v.astype(np.uint32) << 16
+    vf = vf.view(np.float32).astype(np.float64)
+    for h in range(n_q):
+        assert np.array_equal(out[h], vf[h // 8, 0])
+
+
+def test_attention_equal_keys_average_values():
+    """All cached keys equal: every position gets the same weight, so the output is the mean of
+    the value rows (exact rationals: small integers over ctx)."""
+    rng = np.random.default_rng(1)
+    n_q, n_kv, d, ctx = 4, 2, 128, 7
+    q = _bf(rng.integers(-3, 4, (n_q, d)).astype(np.float32))
+    krow = rng.integers(-3, 4, d).astype(np.float32)
+    k = _bf(np.broadcast_to(krow, (n_kv, ctx, d)).copy())
+    vint = rng.integers(-20, 21, (n_kv, ctx, d))
+    v = _bf(vint.astype(np.float32))
+    out = oracle.gqa_decode_attention(q, k, v, ctx)
+    for h in range(n_q):
+        exact = np.array([float(Fraction(int(vint[h // 2, :, j].sum()), ctx)) for j in range(d)])
+        assert np.allclose(out[h], exact, rtol=0, atol=1e-12)
+
+
+def test_attention_two_positions_hand_softmax():
+    """Two positions with scores s0 = 2 * 8 / sqrt(128) and s1 = 0: weights e^s0 / (e^s0 + 1)
+    and 1 / (e^s0 + 1), worked with math.exp.  Pins the 1 / sqrt(head dim) scale and the
+    normalisation."""
+    d = 128
+    q = np.zeros((1, d), np.float32)
+    q[0, 0] = 2.0
+    k = np.zeros((1, 2, d), np.float32)
+    k[0, 0, 0] = 8.0            # score 16 / sqrt(128)
+    v = np.zeros((1, 2, d), np.float32)
+    v[0, 0, :] = 1.0
+    v[0, 1, :] = -3.0
+    out = oracle.gqa_decode_attention(_bf(q), _bf(k), _bf(v), 2)
+    s0 = 16.0 / math.sqrt(128.0)
+    w0 = math.exp(s0) / (math.exp(s0) + 1.0)
+    expect = w0 * 1.0 + (1.0 - w0) * (-3.0)
+    assert abs(out[0, 0] - expect) < 1e-12 and abs(out[0, 5] - expect) < 1e-12
+
+
+def test_attention_position_order_invariance_and_cache_tail():
+    """Permuting the cached positions (keys with their values) leaves the output unchanged,
+    and rows past ctx are never read."""
+    rng = np.random.default_rng(3)
+    n_q, n_kv, d, ctx = 16, 2, 128, 33
+    q = wl.f32_to_bf16_bits(rng.standard_normal((n_q, d), dtype=np.float32))
+    k = wl.f32_to_bf16_bits(rng.standard_normal((n_kv, ctx + 5, d), dtype=np.float32))
+    v = wl.f32_to_bf16_bits(rng.standard_normal((n_kv, ctx + 5, d), dtype=np.float32))
+    base = oracle.gqa_decode_attention(q, k, v, ctx)
+    perm = rng.permutation(ctx)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :ctx] = k[:, perm]
+    v2[:, :ctx] = v[:, perm]
+    k2[:, ctx:] = 0x7FC0  # NaN rows past the cache length
+    v2[:, ctx:] = 0x7FC0
+    got = oracle.gqa_decode_attention(q, k2, v2, ctx)
+    assert np.allclose(got, base, rtol=1e-12, atol=1e-12)
