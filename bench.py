@@ -22,7 +22,8 @@ from a separate pass after each timed region with an event at every stage bounda
 those events themselves cost a few microseconds per step.
 
     python bench.py [--steps K] [--warmup W] [--config prefill512|zipf8192|uniform8192|...]
-                    [--no-secondary] [--no-decode] [--no-long] [--no-cpu-baseline] [--copy-probe]
+                    [--no-secondary] [--no-decode] [--no-long] [--no-attention]
+                    [--no-cpu-baseline] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -72,6 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill512")
     ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the grouped-query decode attention object")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 32768-token layer (single call vs bounded chunks)")
     ap.add_argument("--no-decode", action="store_true",
@@ -333,6 +336,44 @@ def measure_long(cfg, sets, torch, L, dev, wl, chunks=(8192, 16384), reps=3):
     return res
 
 
+def measure_attention(torch, L, dev, wl, reps=200):
+    """Grouped-query decode attention (one query token, 16 query heads on two KV heads, head
+    dim 128) at 4K, 32K and 128K cached positions: time per call over `reps` back-to-back calls
+    (the two kernels, partial and reduce), the cache bytes read per second, and the partial
+    kernel's share of the HBM peak from HIP events around it."""
+    res = {}
+    for name in ("attn4k", "attn32k", "attn128k"):
+        n_q, n_kv, d, ctx = wl.ATTN_CONFIGS[name]
+        q, k, v = wl.make_attention_inputs(n_q, n_kv, d, ctx, seed=0)
+        # four caches, rotated, so that every call reads its cache from HBM (together more
+        # than the 256 MB Infinity Cache at 128K; at 4K and 32K the caches are smaller)
+        ncache = 4
+        qd = dev.to_device(q)
+        ks = [dev.to_device(k) for _ in range(ncache)]
+        vs = [dev.to_device(v) for _ in range(ncache)]
+        shp = L.gqa_shape(n_q, n_kv, d, ctx)
+        ws = torch.empty(L.moe_gqa_decode_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+        out = torch.empty((n_q, d), dtype=torch.int16, device="cuda")
+        for i in range(8):
+            L.moe_gqa_decode_attention(shp, qd, ks[i % ncache], vs[i % ncache], out, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            L.moe_gqa_decode_attention(shp, qd, ks[i % ncache], vs[i % ncache], out, ws)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / reps
+        nbytes = float(wl.attention_bytes(n_q, n_kv, d, ctx))
+        res[name] = {"n_q_heads": n_q, "n_kv_heads": n_kv, "head_dim": d, "ctx": ctx,
+                     "us_per_call": us, "algorithmic_bytes": nbytes,
+                     "gbs": nbytes / (us * 1e-6) / 1e9,
+                     "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "tokens_per_s_one_layer": 1e6 / us}
+        log(f"bench: {name}: {us:.2f} us/call, {res[name]['gbs']:.0f} GB/s of cache "
+            f"({100 * res[name]['hbm_frac']:.1f}% of 8 TB/s)")
+        del ks, vs, ws
+    return res
+
+
 def hbm_ceiling(torch, dev):
     """Measured streaming ceiling: a plain device copy of 1 GiB (2 GiB moved) and a streaming
     read of 2 GiB (torch's sum), best of five each, timed with fence-free HIP events."""
@@ -480,6 +521,13 @@ def main():
                             "weights, single call vs bounded chunks",
                 **measure_long(lcfg, sets, torch, L, dev, wl)}
 
+    attention = None
+    if not args.no_attention:
+        attention = {"workload": "grouped-query decode attention of the pages' full-attention "
+                                 "layers: one query token, 16 query heads on 2 KV heads, head "
+                                 "dim 128 (a reading), bf16 KV cache",
+                     **measure_attention(torch, L, dev, wl)}
+
     ceiling = hbm_ceiling(torch, dev)
     log(f"bench: HBM ceiling copy {ceiling['copy_gbs']:.0f} GB/s, read {ceiling['read_gbs']:.0f} GB/s")
     main_res["roofline"]["frac_of_measured_ceiling"] = (
@@ -521,6 +569,7 @@ def main():
         "zipf8192": secondary,
         "decode": decode,
         "long32768": long,
+        "gqa_decode_attention": attention,
         "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
     }

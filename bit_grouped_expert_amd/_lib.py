@@ -52,6 +52,11 @@ class moe_ws_layout(C.Structure):
                 ("topk_idx", "topk_w", "offsets", "sorted_tok", "slot_row", "act", "y", "total")]
 
 
+class moe_gqa_shape(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("ctx_len", C.c_int32), ("kv_stride", C.c_int64)]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -91,6 +96,10 @@ _SIGS = {
                                             C.POINTER(moe_q4_ffn), C.POINTER(moe_q4_ffn),
                                             C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                             C.c_void_p]),
+    "moe_gqa_decode_workspace_bytes": (C.c_size_t, [C.POINTER(moe_gqa_shape)]),
+    "moe_gqa_decode_attention": (C.c_int, [C.POINTER(moe_gqa_shape), C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                           C.c_void_p]),
 }
 
 
@@ -256,3 +265,20 @@ def moe_layer_forward_noalloc(shp, x, router_w, experts: moe_q4_ffn, shared, out
     sh = C.byref(shared) if shared is not None else None
     _check(lib().moe_layer_forward_noalloc(C.byref(shp), _p(x), _p(router_w), C.byref(experts), sh,
                                            _p(out), _stream(stream)), "moe_layer_forward_noalloc")
+
+
+# ---- grouped-query decode attention
+def gqa_shape(n_q_heads, n_kv_heads, head_dim, ctx_len, kv_stride=None) -> moe_gqa_shape:
+    return moe_gqa_shape(n_q_heads, n_kv_heads, head_dim, ctx_len,
+                         ctx_len if kv_stride is None else kv_stride)
+
+
+def moe_gqa_decode_workspace_bytes(shp: moe_gqa_shape) -> int:
+    return lib().moe_gqa_decode_workspace_bytes(C.byref(shp))
+
+
+def moe_gqa_decode_attention(shp, q, k_cache, v_cache, out, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_gqa_decode_attention(C.byref(shp), _p(q), _p(k_cache), _p(v_cache), _p(out),
+                                          _p(ws), ws_bytes, _stream(stream)),
+           "moe_gqa_decode_attention")

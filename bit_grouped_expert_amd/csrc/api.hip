@@ -719,4 +719,41 @@ moe_status moe_layer_forward_chunked(const moe_shape* shape, const uint16_t* x,
   return MOE_OK;
 }
 
+
+size_t moe_gqa_decode_workspace_bytes(const moe_gqa_shape* s) {
+  if (!s || !attn_supported(s->n_q_heads, s->n_kv_heads, s->head_dim, s->ctx_len, s->kv_stride))
+    return 0;
+  return attn_workspace_bytes(s->n_q_heads, s->n_kv_heads, s->ctx_len);
+}
+
+moe_status moe_gqa_decode_attention(const moe_gqa_shape* s, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!s) return MOE_ERR_NULL;
+  if (!attn_supported(s->n_q_heads, s->n_kv_heads, s->head_dim, s->ctx_len, s->kv_stride))
+    return MOE_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !out || !ws) return MOE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(ws))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < attn_workspace_bytes(s->n_q_heads, s->n_kv_heads, s->ctx_len))
+    return MOE_ERR_WORKSPACE;
+  AttnParams p;
+  p.n_q = s->n_q_heads;
+  p.n_kv = s->n_kv_heads;
+  p.group = s->n_q_heads / s->n_kv_heads;
+  p.ctx = s->ctx_len;
+  p.n_chunks = attn_chunks(s->ctx_len);
+  p.kv_stride = s->kv_stride;
+  p.scale = 1.0f / sqrtf((float)s->head_dim);
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.part_o = (float*)ws;
+  p.part_ml = p.part_o + (size_t)p.n_kv * p.n_chunks * p.group * kAttnHeadDim;
+  p.out = out;
+  launch_attention(p, stream);
+  return launch_status();
+}
+
 }  // extern "C"

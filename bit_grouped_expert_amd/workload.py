@@ -185,3 +185,33 @@ def algorithmic_bytes(cfg: MoEConfig, touched_groups: int) -> int:
 def expert_flops(cfg: MoEConfig) -> int:
     """bf16 expert work: gate_up (2*D*2F) and down (2*F*D) per routed row, k+1 rows per token."""
     return 2 * 3 * cfg.D * cfg.F * (cfg.k + 1) * cfg.T
+
+
+# ---- grouped-query decode attention inputs (the pages' full-attention layers: 16 query
+# heads, two KV heads; head dim 128 is a reading).  Seeded, synthetic: q and the cached keys
+# N(0, 1) (q scaled by q_scale to sharpen the softmax), values N(0, 1), all bf16; positions
+# past ctx (up to kv_stride) hold `pad` (NaN by default, so that a read past the cache shows).
+ATTN_CONFIGS = {
+    # name: (n_q_heads, n_kv_heads, head_dim, ctx_len)
+    "attn32k": (16, 2, 128, 32768),
+    "attn4k": (16, 2, 128, 4096),
+    "attn128k": (16, 2, 128, 131072),
+}
+
+
+def make_attention_inputs(n_q, n_kv, d, ctx, kv_stride=None, seed=0, q_scale=1.0, pad=0x7FC0):
+    """Return (q bf16 bits [n_q, d], k bits [n_kv, kv_stride, d], v bits [n_kv, kv_stride, d])."""
+    stride = ctx if kv_stride is None else kv_stride
+    rng = _rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((n_q, d), dtype=np.float32) * np.float32(q_scale))
+    k = np.full((n_kv, stride, d), pad, dtype=np.uint16)
+    v = np.full((n_kv, stride, d), pad, dtype=np.uint16)
+    k[:, :ctx] = f32_to_bf16_bits(rng.standard_normal((n_kv, ctx, d), dtype=np.float32))
+    v[:, :ctx] = f32_to_bf16_bits(rng.standard_normal((n_kv, ctx, d), dtype=np.float32))
+    return q, k, v
+
+
+def attention_bytes(n_q, n_kv, d, ctx) -> int:
+    """Algorithmic HBM bytes of one decode-attention call: the cached keys and values read once,
+    the query read and the output written (bf16)."""
+    return 2 * n_kv * ctx * d * 2 + 2 * n_q * d * 2

@@ -283,6 +283,38 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x,
                                      const float* router_w, const moe_q4_ffn* experts,
                                      const moe_q4_ffn* shared, uint16_t* out, hipStream_t stream);
 
+/* ---- grouped-query decode attention ----------------------------------------------------
+ * MarkTechPost, "Perplexity open sources Lily, a Rust + Metal inference engine for
+ * Qwen3.6-35B-A3B on Apple Silicon", body paragraph 4 (full-attention layers with
+ * grouped-query attention, 16 query heads and two KV heads, over a growing KV cache) and
+ * paragraph 8 (decode reads the key and value cache; the query heads of one KV head share
+ * a workgroup so that each cached row is loaded once).  One query token:
+ *   out[h] = softmax_j(q[h] . k[g, j] / sqrt(head_dim)) . v[g, j],  j < ctx_len,
+ *   g = h / (n_q_heads / n_kv_heads),
+ * softmax and sums in fp32, output rounded to bf16.  Scale and head mapping are readings. */
+typedef struct {
+  int32_t n_q_heads;  /* query heads; a multiple of n_kv_heads, at most 16 per KV head */
+  int32_t n_kv_heads; /* KV heads, >= 1 */
+  int32_t head_dim;   /* 128 (the only size taken) */
+  int32_t ctx_len;    /* cached positions attended, >= 1 */
+  int64_t kv_stride;  /* positions allocated per KV head in each cache, >= ctx_len */
+} moe_gqa_shape;
+
+/* Workspace bytes of moe_gqa_decode_attention (partial outputs: n_kv_heads x
+ * ceil(ctx_len / 128) x group x 130 floats); 0 for an unsupported shape. */
+size_t moe_gqa_decode_workspace_bytes(const moe_gqa_shape* shape);
+
+/* q: bf16 [n_q_heads, head_dim]; k_cache, v_cache: bf16 [n_kv_heads, kv_stride, head_dim]
+ * (positions 0 .. ctx_len-1 are read, row-major, rows contiguous); out: bf16
+ * [n_q_heads, head_dim]; all device pointers, 16-byte aligned, caller-owned; ws: device
+ * workspace of at least moe_gqa_decode_workspace_bytes.  Two launches on `stream`, no
+ * host synchronisation, no allocation.  Errors: MOE_ERR_SHAPE (unsupported shape),
+ * MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH. */
+moe_status moe_gqa_decode_attention(const moe_gqa_shape* shape, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    uint16_t* out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,3 +168,27 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     bad = shp(D=100)
     assert lib.moe_layer_forward_noalloc(C.byref(bad), A, A, C.byref(ffn), None, A, None) \
         == L.MOE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("bad", [(16, 2, 64, 100, 100), (16, 3, 128, 100, 100), (34, 2, 128, 100, 100),
+                                 (16, 2, 128, 0, 0), (16, 2, 128, 100, 99), (16, 0, 128, 1, 1)])
+def test_gqa_attention_shape_rules(lib, bad):
+    """Unsupported attention shapes: zero workspace and MOE_ERR_SHAPE before any HIP call
+    (head dim other than 128, query heads not a multiple of KV heads, more than 16 per KV head,
+    an empty cache, a stride shorter than the cache, no KV head)."""
+    shp = L.moe_gqa_shape(*bad)
+    assert lib.moe_gqa_decode_workspace_bytes(C.byref(shp)) == 0
+    st = lib.moe_gqa_decode_attention(C.byref(shp), A, A, A, A, A, BIG, None)
+    assert st == L.MOE_ERR_SHAPE
+
+
+def test_gqa_attention_validation(lib):
+    shp = L.gqa_shape(16, 2, 128, 32768)
+    need = lib.moe_gqa_decode_workspace_bytes(C.byref(shp))
+    assert need >= 2 * 256 * 8 * 130 * 4
+    call = lambda q=A, k=A, v=A, o=A, ws=A, n=need: lib.moe_gqa_decode_attention(
+        C.byref(shp), q, k, v, o, ws, n, None)
+    assert call(q=None) == L.MOE_ERR_NULL
+    assert call(ws=None) == L.MOE_ERR_NULL
+    assert call(k=MIS) == L.MOE_ERR_ALIGN
+    assert call(n=need - 1) == L.MOE_ERR_WORKSPACE
