@@ -59,7 +59,12 @@ KERNEL_LABEL = {
 # copy kernel of --copy-probe, read in the same rocprofv3 --pmc runs; the build they were
 # taken on is named in the matching profiles/ summary.  A workload missing here reports
 # traffic null.
-TRAFFIC = {}
+TRAFFIC = {
+    # commit 508afd8 (profiles/gate_up_resident_prefill512_traffic.md)
+    "prefill512": {"fetch_kib": 168130.3, "write_kib": 4608.4,
+                   "copy_fetch_kib": 524300.0, "copy_write_kib": 1048576.0,
+                   "copy_bytes": 1 << 30},
+}
 
 
 def log(*a):
