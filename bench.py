@@ -2,7 +2,7 @@
 """MoE-layer throughput on one MI355X.
 
 A step is one moe_layer_forward (routing, histogram/scan/scatter, grouped gate_up +
-SwiGLU, grouped down, weighted combine) over one batch of synthetic tokens whose inputs
+SwiGLU and grouped down (one launch at 512 tokens), weighted combine) over one batch of synthetic tokens whose inputs
 are resident in HBM.  The headline workload is the 512-token prefill of a
 Qwen3.6-35B-A3B-shaped layer (d_model 2048, 256 experts top-8 + 1 shared expert, d_ff 512,
 int4 weights with bf16 scale and bias per 64); the 8192-token prefill with Zipf-skewed
@@ -13,8 +13,9 @@ distinct weight sets (455 MB each; together more than the 256 MB Infinity Cache)
 that every step streams its weights from HBM.
 
 Prints one JSON line: value = tokens/s at T=512, the roofline of the dominant kernel
-(grouped gate_up, timed inside the timed region with two HIP events that the library
-records on the layer's stream around that stage; the events are created without the
+(the launch that runs grouped gate_up + SwiGLU and down at 512 tokens, the grouped gate_up
+at 8192; timed inside the timed region with two HIP events that the library records on the
+layer's stream around it; the events are created without the
 system-scope fence of a default event) and of the whole layer, the same for the 8192-token
 layer, a measured HBM ceiling (a plain device copy and a streaming read, timed with events)
 and the CPU oracle's rate on a bounded sample.  The per-stage breakdown (stage_us) comes
@@ -44,27 +45,19 @@ RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 METRIC = "MoE-layer tokens/sec at T=512 and T=8192; % of HBM / MFMA roofline"
 SECONDARY = "zipf8192"          # the T=8192 half of the metric, measured in the same run
 
-# the gate_up kernel the library picks for each workload (engine chosen by group size)
+# the dominant kernel for each workload: the grouped gate_up (wide-tile engine), or, where
+# the library runs gate_up and down as one launch (moe_layer_plan: paired), that launch
 KERNEL_LABEL = {
-    "prefill512": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
-    "prefill512_affine": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
-    "decode1": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
-    "decode4": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
-    "uniform8192": "grouped gate_up + SwiGLU (q4_wide_kernel<true, 1>)",
-    "zipf8192": "grouped gate_up + SwiGLU (q4_wide_kernel<true, 1>)",
-    "long32768": "grouped gate_up + SwiGLU (q4_wide_kernel<true, 1>)",
+    "wide": "grouped gate_up + SwiGLU (q4_wide_kernel<true, 1>)",
+    "resident": "grouped gate_up + SwiGLU (q4_resident_kernel<true, 4>)",
+    "paired": "grouped gate_up + SwiGLU then down, one launch (q4_resident_pair_kernel<4, 2>)",
 }
 
-# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the gate_up kernel and of the plain 1 GiB
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel and of the plain 1 GiB
 # copy kernel of --copy-probe, read in the same rocprofv3 --pmc runs; the build they were
 # taken on is named in the matching profiles/ summary.  A workload missing here reports
 # traffic null.
-TRAFFIC = {
-    # commit 508afd8 (profiles/gate_up_resident_prefill512_traffic.md)
-    "prefill512": {"fetch_kib": 168130.3, "write_kib": 4608.4,
-                   "copy_fetch_kib": 524300.0, "copy_write_kib": 1048576.0,
-                   "copy_bytes": 1 << 30},
-}
+TRAFFIC = {}
 
 
 def log(*a):
@@ -103,6 +96,17 @@ def gate_up_algorithmic(cfg, touched_groups):
     wbytes = touched_groups * 2 * cfg.F * cfg.D * (4 + 32 / 64) / 8
     bytes_ = wbytes + cfg.T * cfg.D * 2 + (cfg.k + 1) * cfg.T * cfg.F * 2
     flops = 2.0 * (cfg.k + 1) * cfg.T * 2 * cfg.F * cfg.D
+    return bytes_, flops
+
+
+def pair_algorithmic(cfg, touched_groups):
+    """Bytes and flops of gate_up + SwiGLU and down in one launch: the touched groups'
+    codes + scale + bias (3 F x D weights at 0.5625 B each), x read once, the activations
+    written and read back, y written."""
+    rows = (cfg.k + 1) * cfg.T
+    wbytes = touched_groups * 3 * cfg.F * cfg.D * (4 + 32 / 64) / 8
+    bytes_ = wbytes + cfg.T * cfg.D * 2 + 2 * rows * cfg.F * 2 + rows * cfg.D * 2
+    flops = 2.0 * rows * 3 * cfg.F * cfg.D
     return bytes_, flops
 
 
@@ -167,7 +171,11 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     out = torch.empty((cfg.T, cfg.D), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     nst = L.N_STAGE_EVENTS
-    GU = 2  # events[2]: after the permutation, events[3]: after gate_up
+    GU = 2  # events[2]: after the permutation, events[3]: after gate_up (or after both
+    #         GEMMs when they run as one launch)
+    plan = L.moe_layer_plan(shp)
+    paired = bool(plan.paired)
+    eng = {L.MOE_ENGINE_WIDE: "wide", L.MOE_ENGINE_RESIDENT: "resident"}.get(plan.gemm_engine)
     n_brk = min(steps, 20)
     evs = [[dev.hip_event() for _ in range(nst)] for _ in range(steps)]
     brk = [[dev.hip_event() for _ in range(nst)] for _ in range(n_brk)]
@@ -197,15 +205,17 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     ms_per_step = elapsed * 1e3 / steps
     gu_ms = float(np.mean([dev.hip_elapsed_ms(evs[i][GU], evs[i][GU + 1]) for i in range(steps)]))
     log(f"bench: {cfg.name}: {steps} steps in {elapsed * 1e3:.2f} ms ({ms_per_step:.4f} ms/step), "
-        f"gate_up {gu_ms * 1e3:.1f} us")
+        f"{'gate_up + down (one launch)' if paired else 'gate_up'} {gu_ms * 1e3:.1f} us")
 
     # ---- per-stage breakdown (reporting only, outside the timed region)
     for i in range(n_brk):
         step(i, opts_all[i])
     torch.cuda.synchronize()
     names = ["route", "permute", "gate_up", "down", "combine"]
+    if paired:  # events [3] and [4] both follow the one GEMM launch
+        names = ["route", "permute", "gate_up_and_down", None, "combine"]
     stage_ms = {n: float(np.mean([dev.hip_elapsed_ms(brk[i][j], brk[i][j + 1]) for i in range(n_brk)]))
-                for j, n in enumerate(names)}
+                for j, n in enumerate(names) if n}
     log(f"bench: {cfg.name}: breakdown (events at every stage): "
         + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in stage_ms.items()))
     for row in evs + brk:
@@ -216,7 +226,7 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     offs = ws[lay.offsets:lay.offsets + 4 * (cfg.E + 2)].cpu().numpy().view(np.int32)
     touched = int(np.count_nonzero(np.diff(offs[:cfg.E + 1]))) + 1  # + the shared expert
     counts = np.diff(offs[:cfg.E + 1])
-    gb, gf = gate_up_algorithmic(cfg, touched)
+    gb, gf = (pair_algorithmic if paired else gate_up_algorithmic)(cfg, touched)
     roof = roofline(gb, gf, gu_ms * 1e-3)
     t = TRAFFIC.get(cfg.name)
     if t:
@@ -225,7 +235,7 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
         roof["traffic"] = t["fetch_kib"] * 1024 * scale_f + t["write_kib"] * 1024 * scale_w
     else:
         roof["traffic"] = None
-    roof["kernel"] = KERNEL_LABEL.get(cfg.name, "grouped gate_up + SwiGLU")
+    roof["kernel"] = KERNEL_LABEL["paired" if paired else eng] if (paired or eng) else "grouped gate_up"
     roof["algorithmic_bytes"] = gb
     roof["algorithmic_flops"] = gf
     roof["kernel_us"] = gu_ms * 1e3

@@ -49,7 +49,12 @@ class moe_layer_opts(C.Structure):
 
 class moe_ws_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in
-                ("topk_idx", "topk_w", "offsets", "sorted_tok", "slot_row", "act", "y", "total")]
+                ("topk_idx", "topk_w", "offsets", "sorted_tok", "slot_row", "act", "y", "sync",
+                 "total")]
+
+
+class moe_layer_plan_info(C.Structure):
+    _fields_ = [("gemm_engine", C.c_int32), ("paired", C.c_int32)]
 
 
 class moe_gqa_shape(C.Structure):
@@ -64,6 +69,8 @@ _SIGS = {
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_workspace_bytes": (C.c_size_t, [C.POINTER(moe_shape)]),
     "moe_workspace_layout": (C.c_int, [C.POINTER(moe_shape), C.POINTER(moe_ws_layout)]),
+    "moe_layer_plan": (C.c_int, [C.POINTER(moe_shape), C.c_int32, C.c_int32,
+                                 C.POINTER(moe_layer_plan_info)]),
     "moe_grouped_gemm_q4_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32,
                                                          C.c_int32]),
     "moe_route": (C.c_int, [C.POINTER(moe_shape), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -164,6 +171,13 @@ def moe_workspace_bytes(shp: moe_shape) -> int:
 def moe_workspace_layout(shp: moe_shape) -> moe_ws_layout:
     out = moe_ws_layout()
     _check(lib().moe_workspace_layout(C.byref(shp), C.byref(out)), "moe_workspace_layout")
+    return out
+
+
+def moe_layer_plan(shp: moe_shape, engine: str = "auto", has_shared: bool = True) -> moe_layer_plan_info:
+    out = moe_layer_plan_info()
+    _check(lib().moe_layer_plan(C.byref(shp), ENGINES[engine], int(has_shared), C.byref(out)),
+           "moe_layer_plan")
     return out
 
 

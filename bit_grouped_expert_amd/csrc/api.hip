@@ -83,7 +83,8 @@ int device_cu_count() {
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, xsum_x, xsum_act, xprep, act, y, dec_sync, dec_part, dec_act, total;
+      tile_count, xsum_x, xsum_act, xprep, act, y, sync, dec_part, dec_act, total;
+  int32_t sync_words;  // cleared by the routing kernels of every call
 };
 
 // slots of the decode-sized chain: the distinct touched experts and the shared expert
@@ -121,10 +122,18 @@ Layout make_layout(const moe_shape* s) {
   L.xprep = take((T + 1) * D * 2);  // prepared x, one zero row after the last
   L.act = take((rows_ext + 1) * F * 2);
   L.y = take(rows_ext * D * 2);
-  L.dec_sync = L.dec_part = L.dec_act = 0;
+  // the persistent launches' error word ([0]) and counters: the decode-sized chain's, or
+  // one per tile of the resident pair launch
+  int64_t words = kPairTileBase + max_tiles(rows_ext, (int)E + 1, kResidentBM);
+  if (decode_ok(s)) {
+    const int64_t dw = decode_sync_ints((int)D, (int)F, (int)decode_max_slots(s));
+    words = dw > words ? dw : words;
+  }
+  L.sync_words = (int32_t)words;
+  L.sync = take((size_t)words * 4);
+  L.dec_part = L.dec_act = 0;
   if (decode_ok(s)) {
     const int ms = (int)decode_max_slots(s);
-    L.dec_sync = take((size_t)decode_sync_ints((int)D, (int)F, ms) * 4);
     L.dec_part = take(decode_part_bytes((int)D, (int)F, ms));
     L.dec_act = take(decode_act_bytes((int)F, ms));
   }
@@ -182,6 +191,25 @@ struct GemmCall {
   const int32_t* tile_count;
 };
 
+ResidentParams resident_params(const GemmCall& c) {
+  ResidentParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = c.A;
+  p.a_row_index = c.a_row_index;
+  p.a_rows = c.a_rows;
+  p.main = c.main;
+  p.n_main = c.n_main;
+  p.last = c.last;
+  p.N = c.N;
+  p.K = c.K;
+  p.C = c.C;
+  p.ldc = c.ldc;
+  p.c_perm = c.c_perm;
+  p.tiles = c.tiles;
+  p.tile_count = c.tile_count;
+  return p;
+}
+
 void run_gemm(const GemmCall& c, const GemmPlan& plan, const ResidentPlan& rplan, bool swiglu,
               int64_t rows, int n_groups, int n_cu, hipStream_t stream) {
   const int64_t bound = max_tiles(rows, n_groups, plan.bm);
@@ -203,22 +231,7 @@ void run_gemm(const GemmCall& c, const GemmPlan& plan, const ResidentPlan& rplan
     p.tile_count = c.tile_count;
     launch_wide(p, swiglu, bound, n_cu, stream);
   } else if (plan.eng == ENG_RESIDENT) {
-    ResidentParams p;
-    memset(&p, 0, sizeof(p));
-    p.A = c.A;
-    p.a_row_index = c.a_row_index;
-    p.a_rows = c.a_rows;
-    p.main = c.main;
-    p.n_main = c.n_main;
-    p.last = c.last;
-    p.N = c.N;
-    p.K = c.K;
-    p.C = c.C;
-    p.ldc = c.ldc;
-    p.c_perm = c.c_perm;
-    p.tiles = c.tiles;
-    p.tile_count = c.tile_count;
-    launch_resident(p, rplan, swiglu, stream);
+    launch_resident(resident_params(c), rplan, swiglu, stream);
   } else {
     GemmParams p;
     memset(&p, 0, sizeof(p));
@@ -307,6 +320,7 @@ moe_status moe_workspace_layout(const moe_shape* shape, moe_ws_layout* layout) {
   layout->slot_row = L.slot_row;
   layout->act = L.act;
   layout->y = L.y;
+  layout->sync = L.sync;
   layout->total = L.total;
   return MOE_OK;
 }
@@ -334,7 +348,7 @@ static moe_status route_impl(const moe_shape* shape, const uint16_t* x, const fl
   uint16_t* Rs = at<uint16_t>(ws, L.rsplit);
   float* logits = at<float>(ws, L.logits);
   launch_router(x, router_w, Rs, logits, T, D, E, nullptr, stream);
-  launch_topk(logits, x, router_w, T, D, E, k, gap, topk_idx, topk_w, stream);
+  launch_topk(logits, x, router_w, T, D, E, k, gap, topk_idx, topk_w, nullptr, 0, stream);
   return launch_status();
 }
 
@@ -480,6 +494,30 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const i
   return launch_status();
 }
 
+// The grouped GEMMs of a prefill-sized layer: the engine (from the shapes and the average
+// group size, or forced), the resident plans, and whether gate_up and down run as one
+// launch.  False when a forced engine cannot take the shapes.
+struct LayerGemmPlan {
+  GemmPlan plan;
+  ResidentPlan rp_up, rp_down;
+  bool paired;
+};
+bool plan_layer_gemms(const moe_shape* s, bool has_shared, int32_t engine, int n_cu,
+                      LayerGemmPlan* out) {
+  const int T = s->T, D = s->d_model, E = s->n_experts, k = s->top_k, F = s->d_ff;
+  const int n_groups = E + (has_shared ? 1 : 0);
+  const int rows = T * k + (has_shared ? T : 0);
+  const int64_t rbound = max_tiles(rows, n_groups, kResidentBM);
+  memset(out, 0, sizeof(*out));
+  const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &out->rp_up) &&
+                           resident_plan(D, F, false, rbound, n_cu, &out->rp_down);
+  const bool wide_ok = wide_supported(2 * F, D, true, T) && wide_supported(D, F, false, rows);
+  if (!plan_gemm(engine, rows, n_groups, resident_ok, wide_ok, &out->plan)) return false;
+  out->paired = out->plan.eng == ENG_RESIDENT &&
+                resident_pair_ok(out->rp_up, out->rp_down, 2 * F, D, D, F, rbound);
+  return true;
+}
+
 // planes_ready: the workspace already holds the router's bf16 planes of router_w (a
 // later chunk of moe_layer_forward_chunked)
 static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const float* router_w,
@@ -522,10 +560,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   if (engine == MOE_ENGINE_DECODE || (engine == MOE_ENGINE_AUTO && decode_ok(shape))) {
     // decode-sized chain: router logits (+ prepared x, + the counters cleared), then one
     // persistent launch: plan, gate_up + SwiGLU, down + combine
-    int32_t* sync = at<int32_t>(ws, L.dec_sync);
+    int32_t* sync = at<int32_t>(ws, L.sync);
     mark(0);
     launch_router_small(x, router_w, at<float>(ws, L.logits), T, D, E, at<uint16_t>(ws, L.xprep),
-                        sync, decode_sync_ints(D, F, (int)decode_max_slots(shape)), stream);
+                        sync, L.sync_words, stream);
     mark(1);
     mark(2);
     DecodeParams dp;
@@ -566,15 +604,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   // the GEMM engine depends only on the shapes: chosen first, so that the router can
   // write the prepared copy of x on the way
   const int n_cu = device_cu_count();
-  const int64_t rbound = max_tiles(rows, n_groups, kResidentBM);
-  ResidentPlan rp_up, rp_down;
-  memset(&rp_up, 0, sizeof(rp_up));
-  memset(&rp_down, 0, sizeof(rp_down));
-  const bool resident_ok = resident_plan(2 * F, D, true, rbound, n_cu, &rp_up) &&
-                           resident_plan(D, F, false, rbound, n_cu, &rp_down);
-  const bool wide_ok = wide_supported(2 * F, D, true, T) && wide_supported(D, F, false, rows);
-  GemmPlan plan;
-  if (!plan_gemm(engine, rows, n_groups, resident_ok, wide_ok, &plan)) return MOE_ERR_SHAPE;
+  LayerGemmPlan lp;
+  if (!plan_layer_gemms(shape, has_shared, engine, n_cu, &lp)) return MOE_ERR_SHAPE;
+  const GemmPlan plan = lp.plan;
+  const ResidentPlan rp_up = lp.rp_up, rp_down = lp.rp_down;
   const bool prepared = plan.eng != ENG_GROUPED;
 
   int32_t* idx = at<int32_t>(ws, L.topk_idx);
@@ -594,7 +627,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   mark(0);
   launch_router(x, router_w, at<uint16_t>(ws, L.rsplit), at<float>(ws, L.logits), T, D, E,
                 prepared ? xprep : nullptr, stream, planes_ready);
-  launch_topk(at<float>(ws, L.logits), x, router_w, T, D, E, k, kRefineGap, idx, wts, stream);
+  int32_t* sync = at<int32_t>(ws, L.sync);
+  const bool pair = lp.paired;
+  launch_topk(at<float>(ws, L.logits), x, router_w, T, D, E, k, kRefineGap, idx, wts, sync,
+              L.sync_words, stream);
   mark(1);
   // histogram, scan, scatter (+ identity rows of the shared group), tile map
   const int shared_rows = has_shared ? T : -1;
@@ -630,8 +666,7 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   c.xsum_out = xsum_act;  // grouped: row sums of act for the down GEMM
   c.tiles = tiles;
   c.tile_count = tile_count;
-  run_gemm(c, plan, rp_up, true, rows, n_groups, n_cu, stream);
-  mark(3);
+  GemmCall cu = c;
 
   // down: act rows in order -> y [rows, D]
   c.A = act;
@@ -646,7 +681,16 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
   c.c_perm = 0;
   c.xsum = xsum_act;
   c.xsum_out = nullptr;
-  run_gemm(c, plan, rp_down, false, rows, n_groups, n_cu, stream);
+  if (pair) {
+    // both GEMMs in one launch (each workgroup's down share starts when its gate_up share
+    // is done); the counters it waits on were cleared by the top-k launch
+    launch_resident_pair(resident_params(cu), resident_params(c), rp_up, rp_down, sync, stream);
+    mark(3);
+  } else {
+    run_gemm(cu, plan, rp_up, true, rows, n_groups, n_cu, stream);
+    mark(3);
+    run_gemm(c, plan, rp_down, false, rows, n_groups, n_cu, stream);
+  }
   mark(4);
 
   // combine with the shared expert (rows T*k.. of y)
@@ -654,6 +698,27 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
                  out, T, D, k, stream);
   mark(5);
   return finish();
+}
+
+moe_status moe_layer_plan(const moe_shape* shape, int32_t engine, int32_t has_shared,
+                          moe_layer_plan_info* info) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!info) return MOE_ERR_NULL;
+  if (!layer_engine_valid(engine)) return MOE_ERR_SHAPE;
+  if (engine == MOE_ENGINE_DECODE && !decode_ok(shape)) return MOE_ERR_SHAPE;
+  memset(info, 0, sizeof(*info));
+  if (engine == MOE_ENGINE_DECODE || (engine == MOE_ENGINE_AUTO && decode_ok(shape))) {
+    info->gemm_engine = MOE_ENGINE_DECODE;
+    return MOE_OK;
+  }
+  LayerGemmPlan lp;
+  if (!plan_layer_gemms(shape, has_shared != 0, engine, device_cu_count(), &lp)) return MOE_ERR_SHAPE;
+  info->gemm_engine = lp.plan.eng == ENG_WIDE       ? MOE_ENGINE_WIDE
+                      : lp.plan.eng == ENG_RESIDENT ? MOE_ENGINE_RESIDENT
+                                                    : MOE_ENGINE_GROUPED;
+  info->paired = lp.paired ? 1 : 0;
+  return MOE_OK;
 }
 
 moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const float* router_w,

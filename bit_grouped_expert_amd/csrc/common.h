@@ -83,4 +83,29 @@ __device__ __forceinline__ uint32_t ldg_u32(const void* p) {
   return __builtin_nontemporal_load((const uint32_t*)p);
 }
 
+// Device-scope (agent) accesses, coherent across the XCDs' L2 caches: what one
+// workgroup writes this way and another reads this way within one launch is seen once a
+// completed store is followed by a counter or flag that the reader observes.
+__device__ __forceinline__ int atomic_add_agent(int32_t* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev16(void* p, u32x4_t v) {
+  __hip_atomic_store((uint64_t*)p, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((uint64_t*)p + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4_t load_dev16(const void* p) {
+  const uint64_t lo = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi =
+      __hip_atomic_load((const uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+
 }  // namespace moeq4

@@ -108,23 +108,6 @@ __device__ __forceinline__ int wave_scan_incl(int v, int n) {
   return v;
 }
 
-__device__ __forceinline__ int atomic_add_agent(int32_t* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// device-scope (coherent across the L2 caches) loads and stores
-__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ u32x4_t load_dev16(const void* p) {
-  const uint64_t lo = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t hi =
-      __hip_atomic_load((const uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-}
-
 // ------------------------------------------------------------------------------- staging
 // Weights reach LDS through direct global->LDS loads of 16 bytes per lane: the 64 lanes of
 // one instruction fill 1 KB of LDS, in lane order, from chunks that are contiguous in

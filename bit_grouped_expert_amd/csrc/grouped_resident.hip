@@ -61,6 +61,7 @@ namespace {
 constexpr int KS = 256;            // K per stage: four scale groups (two halves of 128)
 constexpr int SEG_CAP = 48;        // most tiles one workgroup may touch (host-checked)
 constexpr int PART_BYTES = 16384;  // partial sums / output staging
+constexpr int kPairSpinLimit = 1 << 16;  // polls before a pair launch's wait gives up
 
 __host__ __device__ constexpr int part_off(int K) { return 2 * (K / 8) * 256; }
 // row sums X of the tile's activations per 64-wide group as three bf16 pieces whose sum
@@ -112,11 +113,48 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     const int64_t total = (int64_t)cnt * NCH;
     c_begin = (int)(total * rank / G);
     c_end = (int)(total * (rank + 1) / G);
+    if (p.pair_role == 2 && p.pair_wd > 0) {
+      // down phase of a pair launch: split so that every workgroup's gate_up share plus its
+      // down share weighs the same (a chunk weighs its weight rows times K): the down
+      // prefix of rank r is the whole-launch share of r ranks less the gate_up chunks of
+      // those ranks, in down chunks, rounded.  It stays within a few chunks of the gate_up
+      // split and is increasing while a rank's down share exceeds the weight ratio + 2.
+      const int64_t tu = (int64_t)cnt * p.ready_need, wu = p.pair_wu, wd = p.pair_wd;
+      if (total * wd >= (int64_t)G * (wu + 2 * wd)) {
+        auto prefix = [&](int64_t r) -> int64_t {
+          const int64_t a = tu * r / G;
+          return (2 * (r * (wu * tu + wd * total) - (int64_t)G * wu * a) + (int64_t)G * wd) /
+                 (2 * (int64_t)G * wd);
+        };
+        c_begin = (int)prefix(rank);
+        c_end = (int)prefix(rank + 1);
+      }
+    }
     t_first = c_begin / NCH;
     nseg = c_begin < c_end ? (c_end - 1) / NCH - t_first + 1 : 0;
   }
   if (c_begin >= c_end) return;  // uniform, before any barrier
   if (nseg > SEG_CAP) return;    // excluded by the host; never write past the table
+  // a pair launch numbers chunks over the whole tile list (never dealt: excluded by the
+  // host, and both phases see the same tile count, so neither waits on the other here)
+  const int role = p.pair_role;
+  if (role != 0 && dealt) {
+    if (threadIdx.x == 0) atomic_add_agent(p.sync, 1);
+    return;
+  }
+  // chunk i of this workgroup's sequence.  The down phase of a pair launch starts after
+  // the tile it shares with the previous range (that range runs its gate_up part of the
+  // tile last) and ends with it.
+  const int n_ch = c_end - c_begin;
+  int rot = 0;
+  if (role == 2 && c_begin % NCH != 0) {
+    const int first_full = (c_begin / NCH + 1) * NCH;
+    if (first_full < c_end) rot = first_full - c_begin;
+  }
+  auto seq = [&](int i) -> int {
+    const int j = i + rot;
+    return c_begin + (j < n_ch ? j : j - n_ch);
+  };
   // segment k's tile: the k-th of the range, or the k-th dealt to this workgroup
   auto tile_of = [&](int k) -> int { return dealt ? t_lo + jw + WX * k : t_first + k; };
   // tiles and activation row indices of every segment, before any weight load
@@ -139,7 +177,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   };
 
   // ---- weight prefetch cursor (stream of this wavefront's stages over its chunks)
-  int pf_ch = c_begin, pf_s = 0;
+  int pf_i = 0, pf_s = 0;
   const uint32_t* pf_q = nullptr;
   const uint16_t* pf_sc = nullptr;
   const uint16_t* pf_bi = nullptr;
@@ -153,6 +191,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
   const bool sb_hi = sb_g0 + 4 < 4 * NST;
   u32x2_t sb_s[2][2], sb_b[2][2];  // [weight fragment][half]
   auto pf_chunk = [&]() __attribute__((always_inline)) {
+    const int pf_ch = seq(pf_i);
     const int4 t = seg_of(pf_ch);
     const int cin = pf_ch - (pf_ch / NCH) * NCH;
     const int g = t.x;
@@ -196,7 +235,7 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     }
     if (++pf_s == NST) {
       pf_s = 0;
-      if (++pf_ch < c_end) pf_chunk();
+      if (++pf_i < n_ch) pf_chunk();
     }
   };
 
@@ -449,13 +488,66 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     lds_barrier();
   };
 
-  // ---- the first tile's activation rows go through VGPRs, loaded before the weight
-  // prologue: waiting for them then leaves the weight loads in flight (after direct
-  // loads into LDS, the first LDS read would wait for every load issued before it)
   const int per_f = K >> 5;  // 1 KB pieces (32 K of 16 rows) per activation fragment
+  // segment k's activation rows for the whole K: fragment f, 16-byte chunks 4 cb .. 4 cb + 3
+  // of its 16 rows per direct load (1 KB of LDS); device-scope loads in the down phase of
+  // a pair launch (rows written by other workgroups of the launch)
+  auto gather = [&](int k, int nfv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      if (f < nfv) {
+        const int arow = idxt[k * 32 + 16 * f + m];
+        const uint16_t* src = p.A + (int64_t)arow * K + 8 * q;
+        if (role == 2) {
+          for (int cb = wave; cb < per_f; cb += 8)
+            __builtin_amdgcn_global_load_lds(src + 32 * cb, smem + f * A_FRAG + cb * 1024, 16, 0, 16);
+        } else {
+          for (int cb = wave; cb < per_f; cb += 8)
+            __builtin_amdgcn_global_load_lds(src + 32 * cb, smem + f * A_FRAG + cb * 1024, 16, 0, 0);
+        }
+      }
+    }
+  };
+  // pair launch, down phase: one wavefront waits until every gate_up chunk of `tile` has
+  // been counted (bounded: past the limit it counts the failure in sync[0] and goes on)
+  auto wait_tile = [&](int tile) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const uint32_t* cnt = (const uint32_t*)(p.sync + kPairTileBase + tile);
+      int spins = 0;
+      while ((int)load_dev(cnt) < p.ready_need) {
+        if (++spins > kPairSpinLimit) {
+          if (l == 0) atomic_add_agent(p.sync, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    lds_barrier();
+  };
+
   int cur_seg;
-  {
-    const int4 t = seg_of(c_begin);
+  if (role == 2) {
+    // the weight prologue first (it does not depend on the gate_up phase), then the wait,
+    // then the first tile's activations
+    const int c0 = seq(0);
+    const int4 t = seg_of(c0);
+    const int nf0 = t.z > 16 ? 2 : 1;
+    pf_chunk();
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) pf_load(W[d]);
+    for (int o = 16 * tid; o < 3 * XP_PIECE; o += 16 * 512)
+      *(u32x4_t*)(smem + xs_off(K) + o) = u32x4_t{0u, 0u, 0u, 0u};
+    wait_tile(c0 / NCH);
+    gather(t.w, nf0);
+    wait_vmcnt0();
+    lds_barrier();
+    tile_row_sums(nf0);
+    cur_seg = t.w;
+  } else {
+    // the first tile's activation rows go through VGPRs, loaded before the weight
+    // prologue: waiting for them then leaves the weight loads in flight (after direct
+    // loads into LDS, the first LDS read would wait for every load issued before it)
+    const int4 t = seg_of(seq(0));
     const int nf0 = t.z > 16 ? 2 : 1;
     u32x4_t a_first[2][8];
 #pragma unroll
@@ -485,25 +577,17 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
     tile_row_sums(nf0);
     cur_seg = t.w;
   }
-  for (int ch = c_begin; ch < c_end; ++ch) {
+  int pend = -1;  // gate_up phase of a pair launch: tile of the chunk not yet counted
+  for (int ci = 0; ci < n_ch; ++ci) {
+    const int ch = seq(ci);
     const int4 t = seg_of(ch);
     const int k = t.w, row0 = t.y, nrows = t.z;
     const int nfv = nrows > 16 ? 2 : 1;
     const int cin = ch - (ch / NCH) * NCH;
     if (k != cur_seg) {
-      // the tile's activation rows for the whole K: fragment f, 16-byte chunks
-      // 4 cb .. 4 cb + 3 of its 16 rows per direct load (1 KB of LDS)
       lds_barrier();  // every wavefront is done with the previous tile
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        if (f < nfv) {
-          const int arow = idxt[k * 32 + 16 * f + m];
-          const uint16_t* src = p.A + (int64_t)arow * K + 8 * q;
-          for (int cb = wave; cb < per_f; cb += 8)
-            __builtin_amdgcn_global_load_lds(src + 32 * cb, smem + f * A_FRAG + cb * 1024, 16, 0,
-                                             0);
-        }
-      }
+      if (role == 2) wait_tile(ch / NCH);
+      gather(k, nfv);
       wait_vmcnt0();
       lds_barrier();
       tile_row_sums(nfv);
@@ -521,6 +605,13 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
       bias_term(nfv);
     }
 
+    if (role == 1) {
+      // the previous chunk's outputs are complete: this chunk's last stage was loaded after
+      // they were stored, and every wavefront has waited for that stage
+      lds_barrier();
+      if (tid == 0 && pend >= 0) atomic_add_agent(p.sync + kPairTileBase + pend, 1);
+      pend = ch / NCH;
+    }
     // ---- end of chunk: halves of K meet through LDS, then bf16 rows go out
     bool owner = true;
     unsigned char* stg = part + wave * 2048;
@@ -568,9 +659,12 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
           }
         const int r = l >> 1, half = l & 1;
         const int u = CGN * cin + cg;
-        if (r < nrows)
-          *(u32x4_t*)(p.C + (int64_t)(row0 + r) * p.ldc + 16 * u + 8 * half) =
-              *(const u32x4_t*)(cs + r * 16 + 8 * half);
+        if (r < nrows) {
+          uint16_t* dst = p.C + (int64_t)(row0 + r) * p.ldc + 16 * u + 8 * half;
+          const u32x4_t v = *(const u32x4_t*)(cs + r * 16 + 8 * half);
+          if (role == 1) store_dev16(dst, v);
+          else *(u32x4_t*)dst = v;
+        }
       } else {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
@@ -585,12 +679,23 @@ __device__ __forceinline__ void resident_body(const ResidentParams& p, unsigned 
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int r = (64 * pp + l) >> 2, piece = l & 3;
-          if (r < nrows)
-            *(u32x4_t*)(p.C + (int64_t)(row0 + r) * p.ldc + col0 + 8 * piece) =
-                *(const u32x4_t*)(cs + r * 32 + 8 * piece);
+          if (r < nrows) {
+            uint16_t* dst = p.C + (int64_t)(row0 + r) * p.ldc + col0 + 8 * piece;
+            const u32x4_t v = *(const u32x4_t*)(cs + r * 32 + 8 * piece);
+            if (role == 1) store_dev16(dst, v);
+            else *(u32x4_t*)dst = v;
+          }
         }
       }
     }
+    // keeps the stores ahead of the next chunk's loads in program order
+    asm volatile("" ::: "memory");
+  }
+  if (role == 1) {
+    // the last chunk: wait for the stores themselves
+    wait_vmcnt0();
+    lds_barrier();
+    if (tid == 0 && pend >= 0) atomic_add_agent(p.sync + kPairTileBase + pend, 1);
   }
 }
 
@@ -611,7 +716,36 @@ __global__ __launch_bounds__(512, 1) void q4_resident_kernel(ResidentParams p) {
   else resident_body<SWIGLU, NST, 0>(p, smem_dyn);
 }
 
+// gate_up (+ SwiGLU) then down in one launch: each workgroup runs its gate_up range, then
+// its down range over the same tiles (the chunk counts per tile are equal at the layer's
+// shapes, so both ranges cover about the same rows), so that the down weights start
+// streaming as soon as a workgroup's gate_up share is done instead of after the slowest
+// workgroup's.  Every workgroup must be resident at once: the grid is one workgroup per
+// compute unit (the LDS of one takes a whole unit).
+template <int NU, int ND>
+__global__ __launch_bounds__(512, 1) void q4_resident_pair_kernel(ResidentParams up, ResidentParams dn) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_dyn[lds_bytes(kResidentMaxK)];
+  const int l = threadIdx.x & 63;
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)(4 * (l >> 4)), (uint32_t)(4 * (l >> 4) + 2),
+                                                  false, false);
+  const int gs = __builtin_amdgcn_readfirstlane((int)(r[0] >> 3));
+  if (gs) {
+    resident_body<true, NU, 1>(up, smem_dyn);
+    lds_barrier();
+    resident_body<false, ND, 1>(dn, smem_dyn);
+  } else {
+    resident_body<true, NU, 0>(up, smem_dyn);
+    lds_barrier();
+    resident_body<false, ND, 0>(dn, smem_dyn);
+  }
+}
+
 namespace {
+
+template <int NU, int ND>
+void launch_pair_one(const ResidentParams& up, const ResidentParams& dn, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((q4_resident_pair_kernel<NU, ND>), dim3(grid), dim3(512), 0, s, up, dn);
+}
 
 template <bool SWIGLU, int NST>
 void launch_one(const ResidentParams& p, int grid, hipStream_t s) {
@@ -664,6 +798,45 @@ void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hi
   p.ksplit = plan.ksplit;
   if (swiglu) launch_nst<true>(p, plan.stages, plan.grid, s);
   else launch_nst<false>(p, plan.stages, plan.grid, s);
+}
+
+bool resident_pair_ok(const ResidentPlan& up, const ResidentPlan& down, int N_up, int K_up, int N_dn,
+                      int K_dn, int64_t n_tiles_bound) {
+  if (up.grid != down.grid || up.grid < 8) return false;
+  if (up.stages != 2 && up.stages != 4) return false;
+  if (down.stages != 1 && down.stages != 2) return false;
+  // never the dealt mode (at least eight tiles per workgroup)
+  if (n_tiles_bound <= 0 || n_tiles_bound >= 8 * (int64_t)up.grid) return false;
+  // the weighted down split gives a workgroup at most its even share plus the weight ratio
+  // plus two chunks: its tiles must fit the segment table
+  const int64_t cr_up = 32 * (8 / up.ksplit), cr_dn = 32 * (8 / down.ksplit);
+  const int64_t nch_dn = N_dn / cr_dn;
+  const int64_t ratio = (cr_up * K_up + cr_dn * K_dn - 1) / (cr_dn * K_dn);
+  const int64_t per_wg = (n_tiles_bound * nch_dn + up.grid - 1) / up.grid + ratio + 2;
+  (void)N_up;
+  return (per_wg - 1) / nch_dn + 2 <= SEG_CAP;
+}
+
+void launch_resident_pair(ResidentParams up, ResidentParams down, const ResidentPlan& pu,
+                          const ResidentPlan& pd, int32_t* sync, hipStream_t s) {
+  up.ksplit = pu.ksplit;
+  down.ksplit = pd.ksplit;
+  up.pair_role = 1;
+  down.pair_role = 2;
+  up.sync = down.sync = sync;
+  up.ready_need = down.ready_need = 0;
+  // a tile is ready for the down phase once all its gate_up chunks are counted
+  down.ready_need = up.N / (32 * (8 / pu.ksplit));
+  // chunk weights (weight rows times K) of the two phases, for the balanced down split
+  down.pair_wu = 32 * (8 / pu.ksplit) * up.K;
+  down.pair_wd = 32 * (8 / pd.ksplit) * down.K;
+  if (pu.stages == 4) {
+    if (pd.stages == 2) launch_pair_one<4, 2>(up, down, pu.grid, s);
+    else launch_pair_one<4, 1>(up, down, pu.grid, s);
+  } else {
+    if (pd.stages == 2) launch_pair_one<2, 2>(up, down, pu.grid, s);
+    else launch_pair_one<2, 1>(up, down, pu.grid, s);
+  }
 }
 
 }  // namespace moeq4

@@ -26,8 +26,9 @@ void launch_router_small(const uint16_t* x, const float* R, float* L, int T, int
                          uint16_t* xprep, int32_t* zero, int n_zero, hipStream_t s);
 void launch_router(const uint16_t* x, const float* R, uint16_t* Rs, float* L, int T, int D, int E,
                    uint16_t* xprep, hipStream_t s, bool planes_ready = false);
+// also clears n_zero words at `zero` (nullable): a later launch's counters
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
-                 float tau, int32_t* idx, float* w, hipStream_t s);
+                 float tau, int32_t* idx, float* w, int32_t* zero, int n_zero, hipStream_t s);
 
 // ---------------------------------------------------------------- permutation
 constexpr int kChunkTokens = 256;  // tokens per histogram / scatter chunk
@@ -125,8 +126,19 @@ struct ResidentParams {
   const int4* tiles;
   const int32_t* tile_count;
   int32_t ksplit;             // set by launch_resident
+  // One launch for gate_up then down (launch_resident_pair), else all zero.  Role 1 (the
+  // gate_up phase): outputs go out with device-scope stores, and every finished chunk adds
+  // one to sync[kPairTileBase + tile].  Role 2 (the down phase): before reading tile t's
+  // activations (device-scope loads) it waits until that count reaches ready_need, and it
+  // takes its chunk range starting after the tile it shares with the previous range.  A
+  // wait that gives up adds one to sync[0].
+  int32_t pair_role;
+  int32_t ready_need;
+  int32_t pair_wu, pair_wd;   // role 2: weights of a gate_up and a down chunk
+  int32_t* sync;
 };
 constexpr int kResidentMaxStages = 4;  // 256-K stages per wavefront and chunk
+constexpr int kPairTileBase = 64;      // sync words before the per-tile counters
 struct ResidentPlan {
   int ksplit;  // 1: eight column groups over the whole K; 2: four column groups x two K halves
   int stages;  // 256-K stages per wavefront and chunk (K / 256 / ksplit)
@@ -137,6 +149,16 @@ struct ResidentPlan {
 // tiles per workgroup for n_tiles_bound)
 bool resident_plan(int N, int K, bool swiglu, int64_t n_tiles_bound, int n_cu, ResidentPlan* out);
 void launch_resident(ResidentParams p, const ResidentPlan& plan, bool swiglu, hipStream_t s);
+// gate_up (+ SwiGLU) and down as one launch: every workgroup runs its gate_up range, then
+// its down range, whose tiles wait on the gate_up chunks that write their activations.
+// Needs sync[0 .. kPairTileBase + n_tiles_bound) zero at the launch.  resident_pair_ok is
+// false where the pair does not apply: the two plans differ in grid, a stage count is not
+// compiled for it, the tile bound reaches the dealt mode (8 tiles per workgroup), or a
+// workgroup's down share could overflow its segment table.
+bool resident_pair_ok(const ResidentPlan& up, const ResidentPlan& down, int N_up, int K_up, int N_dn,
+                      int K_dn, int64_t n_tiles_bound);
+void launch_resident_pair(ResidentParams up, ResidentParams down, const ResidentPlan& pu,
+                          const ResidentPlan& pd, int32_t* sync, hipStream_t s);
 
 // Parameters of the wide-tile engine.
 struct WideParams {

@@ -503,14 +503,17 @@ void launch_router_logits(const uint16_t* x, const uint16_t* Rs, float* L, int T
 }
 
 // ---------------------------------------------------------------------------- top-k
-// One wavefront per token; E <= 64 * MAXC.
+// One wavefront per token; E <= 64 * MAXC.  The workgroups also clear n_zero words at
+// `zero` (a later launch's counters).
 template <int MAXC>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
                                                    const uint16_t* __restrict__ x,
                                                    const float* __restrict__ R, int T, int D,
                                                    int E, int k, float tau,
                                                    int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out) {
+                                                   float* __restrict__ w_out,
+                                                   int32_t* __restrict__ zero, int n_zero) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_zero; i += gridDim.x * 256) zero[i] = 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // no barriers below
@@ -524,14 +527,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
 }
 
 void launch_topk(const float* L, const uint16_t* x, const float* R, int T, int D, int E, int k,
-                 float tau, int32_t* idx, float* w, hipStream_t s) {
+                 float tau, int32_t* idx, float* w, int32_t* zero, int n_zero, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
+  if (!zero) n_zero = 0;
   if (E <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w, zero, n_zero);
   else if (E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w, zero, n_zero);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, L, x, R, T, D, E, k, tau, idx, w, zero,
+                       n_zero);
 }
 
 // ---------------------------------------------------------------------------- few tokens

@@ -98,7 +98,9 @@ typedef enum {
   MOE_ENGINE_AUTO = 0,
   MOE_ENGINE_GROUPED = 1,  /* any N % 64, K % 64: tiles of up to 32 rows */
   MOE_ENGINE_RESIDENT = 2, /* K % 256 == 0, K <= 2048: tiles of up to 32 rows held in LDS
-                              over the whole K while the weights stream (small groups) */
+                              over the whole K while the weights stream (small groups); in
+                              the layer calls gate_up and down run as one launch where
+                              moe_layer_plan reports paired */
   MOE_ENGINE_WIDE = 3,     /* K % 256 == 0, K <= 2048, N % 256 == 0: tiles of up to 128
                               rows (large groups) */
   MOE_ENGINE_DECODE = 4    /* moe_layer_forward_ex only: the decode-sized chain (T <= 16,
@@ -117,7 +119,8 @@ typedef struct {
                          NULL) recorded on `stream`: [0] before routing, [1] after routing
                          (logits, top-k), [2] after the permutation and tile map, [3] after
                          the grouped gate_up + SwiGLU, [4] after the grouped down, [5] after
-                         the combine */
+                         the combine; when the two GEMMs run as one launch (moe_layer_plan's
+                         paired), [3] and [4] both follow it */
 } moe_layer_opts;
 
 /* Byte offsets of the intermediates moe_layer_forward leaves in its workspace
@@ -132,6 +135,9 @@ typedef struct {
                         by the decode-sized chain) */
   size_t y;          /* bf16  [(k+1)T, D] expert outputs; rows kT.. = shared expert (not
                         written by the decode-sized chain, which never stores them) */
+  size_t sync;       /* int32 counters of the persistent launches (cleared by the call's
+                        routing kernels); word 0 counts waits that gave up their bound,
+                        and is 0 after every correct call */
   size_t total;      /* == moe_workspace_bytes */
 } moe_ws_layout;
 
@@ -245,6 +251,22 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_sorted, const i
 moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, const float* router_w,
                              const moe_q4_ffn* experts, const moe_q4_ffn* shared, uint16_t* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* What moe_layer_forward_ex does for `shape` with options engine `engine` and a shared
+ * expert or not (has_shared 0/1), on the current device.  Host-only, pure.  [MTP] para. 6
+ * (the expert GEMMs walk tiles of expert rows through a block map).
+ *   gemm_engine: MOE_ENGINE_GROUPED, _RESIDENT or _WIDE for the grouped GEMMs, or
+ *                MOE_ENGINE_DECODE for the decode-sized chain;
+ *   paired:      1 when gate_up (+ SwiGLU) and down run as one launch (resident engine:
+ *                each workgroup's down share starts when its gate_up share is done); the
+ *                stage events [3] and [4] are then both recorded after that launch.
+ * MOE_ERR_SHAPE where moe_layer_forward_ex would return it for the engine. */
+typedef struct {
+  int32_t gemm_engine;
+  int32_t paired;
+} moe_layer_plan_info;
+moe_status moe_layer_plan(const moe_shape* shape, int32_t engine, int32_t has_shared,
+                          moe_layer_plan_info* info);
 
 /* moe_layer_forward with options (engine choice, stage events; NULL = defaults).  Same
  * validation and results; opts->reserved must be 0 and opts->engine a moe_engine (else

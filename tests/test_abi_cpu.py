@@ -72,12 +72,35 @@ def test_workspace_bytes_monotone_and_layout(lib):
         assert all(o % 256 == 0 for o in offs)
         assert offs == sorted(offs) and lay.total == n
         assert lay.y + (9 * T) * 2048 * 2 <= n
+        # the counters of the persistent launches: one word per tile past the first 64
+        assert lay.sync % 256 == 0 and lay.sync >= lay.y + (9 * T) * 2048 * 2
+        assert lay.sync + 4 * (64 + (9 * T) // 32 + 257) <= n
     assert L.moe_grouped_gemm_q4_workspace_bytes(0, 10, 10, 64) == 0
     assert L.moe_grouped_gemm_q4_workspace_bytes(4, 10, 10, 96) == 0       # K % 64 != 0
     assert L.moe_grouped_gemm_q4_workspace_bytes(4, 10, -1, 64) == 0
     need = L.moe_grouped_gemm_q4_workspace_bytes(257, 4608, 512, 2048)
     assert need >= (4608 // 32 + 257) * 16 + 512 * 32 * 4       # tile map + row sums of A
     assert L.moe_grouped_gemm_q4_workspace_bytes(257, 4608, 1024, 2048) > need
+
+
+def test_layer_plan(lib):
+    """The engine and launch shape the layer calls take (host-only; without a GPU the
+    compute-unit count defaults to 256)."""
+    p = L.moe_layer_plan(shp(T=512))
+    assert (p.gemm_engine, p.paired) == (L.MOE_ENGINE_RESIDENT, 1)
+    p = L.moe_layer_plan(shp(T=8192))
+    assert (p.gemm_engine, p.paired) == (L.MOE_ENGINE_WIDE, 0)
+    assert L.moe_layer_plan(shp(T=1)).gemm_engine == L.MOE_ENGINE_DECODE
+    p = L.moe_layer_plan(shp(T=1), "resident")
+    assert (p.gemm_engine, p.paired) == (L.MOE_ENGINE_RESIDENT, 1)
+    p = L.moe_layer_plan(shp(T=512), "grouped")
+    assert (p.gemm_engine, p.paired) == (L.MOE_ENGINE_GROUPED, 0)
+    # d_ff = 128: no resident plan (K = F must be a multiple of 256)
+    assert L.moe_layer_plan(shp(T=512, F=128)).gemm_engine == L.MOE_ENGINE_GROUPED
+    with pytest.raises(L.MoEError):
+        L.moe_layer_plan(shp(T=512, F=128), "resident")
+    with pytest.raises(L.MoEError):
+        L.moe_layer_plan(shp(T=512), "decode")
 
 
 def ffn(q=A, s=A, b=A):

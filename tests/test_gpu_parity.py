@@ -380,6 +380,8 @@ def _layer_gpu(torch, cfg, x, router, lw, with_shared=True, engine="auto"):
         "sorted_tok": grab(lay.sorted_tok, (cfg.k + 1) * cfg.T, np.int32),
         "slot_row": grab(lay.slot_row, cfg.T * cfg.k, np.int32),
     }
+    # the persistent launches' waits all ended before their bound
+    assert grab(lay.sync, 1, np.int32)[0] == 0
     return dev.to_host(out, np.uint16), inter
 
 
