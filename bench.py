@@ -57,7 +57,12 @@ KERNEL_LABEL = {
 # copy kernel of --copy-probe, read in the same rocprofv3 --pmc runs; the build they were
 # taken on is named in the matching profiles/ summary.  A workload missing here reports
 # traffic null.
-TRAFFIC = {}
+TRAFFIC = {
+    # commit a62cd4d (profiles/grouped_gemms_pair_prefill512_traffic.md)
+    "prefill512": {"fetch_kib": 248885.8, "write_kib": 27770.9,
+                   "copy_fetch_kib": 524300.0, "copy_write_kib": 1048576.0,
+                   "copy_bytes": 1 << 30},
+}
 
 
 def log(*a):
