@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ L,
   if (t >= T) return;  // no barriers below
   int e;
   float w;
-  topk_token<MAXC>(L + (int64_t)t * E, x + (int64_t)t * D, R, D, E, k, tau, e, w);
+  topk_token<MAXC, 8, 2>(L + (int64_t)t * E, x + (int64_t)t * D, R, D, E, k, tau, e, w);
   if (lane < k) {
     idx_out[(int64_t)t * k + lane] = e;
     w_out[(int64_t)t * k + lane] = w;

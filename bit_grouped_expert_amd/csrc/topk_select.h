@@ -77,6 +77,53 @@ __device__ __forceinline__ uint32_t wave_all_reduce(uint32_t v, Op op) {
   return op((uint32_t)b[0], (uint32_t)b[1]);
 }
 
+// Sum over the wavefront in fp64 with the same bits on every lane: partners of lane i are
+// i ^ 1 and i ^ 2 (quad permutes), then the other quad of its half-row and the other half
+// of its row (half-row and row mirrors, which pair whole quads and halves once the values
+// are uniform within them), then the neighbouring row and half (lane swaps).  Each step
+// adds two values that every lane of the pair holds, in either order, so all lanes agree.
+__device__ __forceinline__ double dpp_partner_f64(double v, int ctrl_tag) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  switch (ctrl_tag) {
+    case 0:
+      lo = __builtin_amdgcn_update_dpp(0, lo, 0xb1, 0xf, 0xf, false);  // quad [1,0,3,2]
+      hi = __builtin_amdgcn_update_dpp(0, hi, 0xb1, 0xf, 0xf, false);
+      break;
+    case 1:
+      lo = __builtin_amdgcn_update_dpp(0, lo, 0x4e, 0xf, 0xf, false);  // quad [2,3,0,1]
+      hi = __builtin_amdgcn_update_dpp(0, hi, 0x4e, 0xf, 0xf, false);
+      break;
+    case 2:
+      lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xf, 0xf, false);  // row_half_mirror
+      hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xf, 0xf, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xf, 0xf, false);  // row_mirror
+      hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xf, 0xf, false);
+      break;
+  }
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_partner_f64(v, 0);
+  v += dpp_partner_f64(v, 1);
+  v += dpp_partner_f64(v, 2);
+  v += dpp_partner_f64(v, 3);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const auto l16 = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  const double a = __longlong_as_double((long long)(((uint64_t)h16[0] << 32) | l16[0]));
+  const double b = __longlong_as_double((long long)(((uint64_t)h16[1] << 32) | l16[1]));
+  v = a + b;
+  const uint64_t w = (uint64_t)__double_as_longlong(v);
+  const auto l32 = __builtin_amdgcn_permlane32_swap((uint32_t)w, (uint32_t)w, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap((uint32_t)(w >> 32), (uint32_t)(w >> 32), false, false);
+  const double c = __longlong_as_double((long long)(((uint64_t)h32[0] << 32) | l32[0]));
+  const double d = __longlong_as_double((long long)(((uint64_t)h32[1] << 32) | l32[1]));
+  return c + d;
+}
+
 // (value, expert) pair order: larger value first, then lower expert id.
 struct Cand {
   double v;
@@ -90,7 +137,9 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
 // router R [E, D] for the fp64 rescoring).  On lane j < k: out_e = the j-th expert
 // (descending logit), out_w = its routing weight (softmax over the k selected fp32
 // logits); other lanes get out_w = 0.  No barriers: callable by any wavefront alone.
-template <int MAXC>
+// Rescoring passes (E <= 256) take NB experts at a time (2 or 4) with RS 1 KB steps of x
+// and their R rows in flight; RS = 8 covers d_model 2048 in one round of loads.
+template <int MAXC, int RS = 4, int NB = 4>
 __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
                                            const uint16_t* __restrict__ xt,
                                            const float* __restrict__ R, int D, int E, int k,
@@ -158,10 +207,11 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
     sk[MAXC - 1] = pop ? 0u : sk[MAXC - 1];
   }
 
-  // fp64 logits of up to four experts (uniform ids ce[0 .. nb-1]; slots past nb repeat
-  // ce[0]): lane d sums d, d + 64, ... in order (several steps of loads in flight), then a
-  // fixed butterfly adds the lanes, so every lane gets the four sums.  bf16 x fp32
-  // products are exact in fp64.
+  // fp64 logits of up to NB experts (uniform ids ce[0 .. nb-1]; slots past nb repeat
+  // ce[0]) (E > 256: always four): lane d sums d, d + 64, ... in order (several steps of
+  // loads in flight), then a fixed butterfly adds the lanes, so every lane gets the sums.
+  // bf16 x fp32 products are exact in fp64.
+  constexpr int NBE = MAXC >= 16 ? 4 : NB;
   auto exact4 = [&](const int* ce, int nb, double* out) __attribute__((always_inline)) {
     const float* Rr[4];
 #pragma unroll
@@ -186,19 +236,18 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
       }
     } else {
       // lane l takes d = 256 s + 4 l .. 4 l + 3 of step s (D % 64 == 0: a step's four d
-      // are all in range or all out), 16-byte loads of each row, four steps in flight
-      // (half the dependent rounds of single-element loads at the same registers per d)
-      constexpr int UN = 4;
+      // are all in range or all out), 16-byte loads of each row, RS steps in flight
+      constexpr int UN = RS;
       for (int d0 = 0; d0 < D; d0 += 256 * UN) {
         u32x2_t xv[UN];
-        f32x4_t rv[UN][4];
+        f32x4_t rv[UN][NBE];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
           const int dd = d0 + 256 * u + 4 * lane;
           const int d = dd < D ? dd : D - 4;
           xv[u] = *(const u32x2_t*)(xt + d);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) rv[u][j] = *(const f32x4_t*)(Rr[j] + d);
+          for (int j = 0; j < NBE; ++j) rv[u][j] = *(const f32x4_t*)(Rr[j] + d);
           if (dd >= D) xv[u] = u32x2_t{0u, 0u};
         }
 #pragma unroll
@@ -208,12 +257,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sj[j] += (double)xf[c] * (double)rv[u][j][c];
+            for (int j = 0; j < NBE; ++j) sj[j] += (double)xf[c] * (double)rv[u][j][c];
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = wave_sum_f64(sj[j]);
+    for (int j = 0; j < NBE; ++j) out[j] = wave_sum_f64_dpp(sj[j]);
   };
 
   if (k < E) {
@@ -242,7 +291,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
         double sums[4];
         exact4(ce, nb, sums);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NBE; ++j) {
           const double sum = sums[j];
           if (j < nb && (ce[j] & 63) == lane) {
 #pragma unroll
@@ -261,7 +310,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
           // ce[nb] = c * 64 + b, without a dynamically indexed array
 #pragma unroll
           for (int j = 0; j < 4; ++j) ce[j] = j == nb ? c * 64 + b : ce[j];
-          if (++nb == 4) flush();
+          if (++nb == NBE) flush();
         }
       }
       if (nb > 0) flush();
@@ -318,11 +367,11 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
           ce[j] = j == nb ? e : ce[j];
           cl[j] = j == nb ? b : cl[j];
         }
-        if (++nb == 4 || runs == 0) {
+        if (++nb == NBE || runs == 0) {
           double sums[4];
           exact4(ce, nb, sums);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NBE; ++j)
             if (j < nb && cl[j] == lane) ex = sums[j];
           nb = 0;
         }
