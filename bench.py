@@ -358,9 +358,9 @@ def measure_long(cfg, sets, torch, L, dev, wl, chunks=(8192, 16384), reps=3):
 
 def measure_attention(torch, L, dev, wl, reps=200):
     """Grouped-query decode attention (one query token, 16 query heads on two KV heads, head
-    dim 128) at 4K, 32K and 128K cached positions: time per call over `reps` back-to-back calls
-    (the two kernels, partial and reduce), the cache bytes read per second, and the partial
-    kernel's share of the HBM peak from HIP events around it."""
+    dim 128) at 4K, 32K and 128K cached positions: time per call (the two kernels, partial and
+    reduce) as replays of a captured graph of eight calls (and, for reference, over `reps`
+    calls issued one by one), and the cache bytes read per second."""
     res = {}
     for name in ("attn4k", "attn32k", "attn128k"):
         n_q, n_kv, d, ctx = wl.ATTN_CONFIGS[name]
@@ -374,22 +374,53 @@ def measure_attention(torch, L, dev, wl, reps=200):
         shp = L.gqa_shape(n_q, n_kv, d, ctx)
         ws = torch.empty(L.moe_gqa_decode_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
         out = torch.empty((n_q, d), dtype=torch.int16, device="cuda")
+        cur = torch.cuda.current_stream()
+
+        def call(i, stream):
+            L.moe_gqa_decode_attention(shp, qd, ks[i % ncache], vs[i % ncache], out, ws,
+                                       stream=stream)
         for i in range(8):
-            L.moe_gqa_decode_attention(shp, qd, ks[i % ncache], vs[i % ncache], out, ws)
+            call(i, cur)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(reps):
-            L.moe_gqa_decode_attention(shp, qd, ks[i % ncache], vs[i % ncache], out, ws)
+            call(i, cur)
         torch.cuda.synchronize()
-        us = (time.perf_counter() - t0) * 1e6 / reps
+        eager_us = (time.perf_counter() - t0) * 1e6 / reps
+        # the same calls as replays of one captured graph of eight (two per cache): the GPU's
+        # time per call without the host's launch cost
+        per_graph = 2 * ncache
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            for i in range(per_graph):
+                call(i, side)
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for i in range(per_graph):
+                call(i, cap)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, reps // per_graph)
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (n_rep * per_graph)
+        del g
         nbytes = float(wl.attention_bytes(n_q, n_kv, d, ctx))
         res[name] = {"n_q_heads": n_q, "n_kv_heads": n_kv, "head_dim": d, "ctx": ctx,
-                     "us_per_call": us, "algorithmic_bytes": nbytes,
+                     "us_per_call": us, "eager_us_per_call": eager_us,
+                     "algorithmic_bytes": nbytes,
                      "gbs": nbytes / (us * 1e-6) / 1e9,
                      "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                      "tokens_per_s_one_layer": 1e6 / us}
-        log(f"bench: {name}: {us:.2f} us/call, {res[name]['gbs']:.0f} GB/s of cache "
-            f"({100 * res[name]['hbm_frac']:.1f}% of 8 TB/s)")
+        log(f"bench: {name}: {us:.2f} us/call as graph replays ({eager_us:.2f} eager), "
+            f"{res[name]['gbs']:.0f} GB/s of cache ({100 * res[name]['hbm_frac']:.1f}% of 8 TB/s)")
         del ks, vs, ws
     return res
 

@@ -814,6 +814,7 @@ moe_status moe_gqa_decode_attention(const moe_gqa_shape* s, const uint16_t* q,
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
+  attn_partition(&p, device_cu_count());
   p.part_o = (float*)ws;
   p.part_ml = p.part_o + (size_t)p.n_kv * p.n_chunks * p.group * kAttnHeadDim;
   p.out = out;

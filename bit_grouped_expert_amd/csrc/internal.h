@@ -225,22 +225,25 @@ void launch_decode_layer(const DecodeParams& p, int max_slots, hipStream_t s);
 
 // ---------------------------------------------------------------- decode attention
 // Grouped-query attention of one query token over a bf16 KV cache (attention.hip): a
-// partial launch per (KV head, 128 cached positions) and a reduce launch per query head.
+// partial launch over runs of 128-position chunks per KV head and a reduce launch per
+// query head.
 constexpr int kAttnHeadDim = 128;
 struct AttnParams {
   int32_t n_q, n_kv, group, ctx, n_chunks;
+  int32_t per_part, n_part;  // chunks per partial, partials per KV head (attn_partition)
   int64_t kv_stride;      // positions allocated per KV head
   float scale;            // 1 / sqrt(head dim)
   const uint16_t* q;      // bf16 [n_q, 128]
   const uint16_t* k;      // bf16 [n_kv, kv_stride, 128]
   const uint16_t* v;      // bf16 [n_kv, kv_stride, 128]
-  float* part_o;          // [n_kv, n_chunks, group, 128] unnormalised partial outputs
-  float* part_ml;         // [n_kv, n_chunks, group, 2] partial max and sum
+  float* part_o;          // [n_kv, n_part, group, 128] unnormalised partial outputs
+  float* part_ml;         // [n_kv, n_part, group, 2] partial max and sum
   uint16_t* out;          // bf16 [n_q, 128]
 };
 bool attn_supported(int n_q, int n_kv, int head_dim, int ctx, int64_t kv_stride);
 int attn_chunks(int ctx);
 size_t attn_workspace_bytes(int n_q, int n_kv, int ctx);
+void attn_partition(AttnParams* p, int n_cu);
 void launch_attention(const AttnParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- combine

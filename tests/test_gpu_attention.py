@@ -54,10 +54,11 @@ def _check(got, ref, what):
                            f"{float((err - bound).max()):.3e} (rms {rms:.3e})")
 
 
-@pytest.mark.parametrize("ctx", [1, 5, 127, 128, 129, 1000, 4096, 32768])
+@pytest.mark.parametrize("ctx", [1, 5, 127, 128, 129, 1000, 4096, 32768, 100000, 131072])
 def test_attention_parity_ctx(torch_cuda, ctx):
-    """16 query heads on two KV heads (the pages' layers), context from one position to 32K:
-    a partial chunk, exact chunk multiples and one past, every output element."""
+    """16 query heads on two KV heads (the pages' layers), context from one position to 128K:
+    a partial chunk, exact chunk multiples and one past, runs of several chunks per
+    workgroup (a ragged last run at 100000), every output element."""
     say(f"gqa attention 16/2 ctx={ctx}")
     got, ref = _run(torch_cuda, 16, 2, ctx, seed=ctx)
     _check(got, ref, f"ctx {ctx}")
@@ -95,3 +96,58 @@ def test_attention_repeatable(torch_cuda):
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_attention_sharp_softmax_long_runs(torch_cuda):
+    """A query scaled by 8 over 40000 positions: each workgroup combines several chunks whose
+    maxima differ widely, so the running maximum rises within a run and the sums are rescaled."""
+    say("gqa attention ctx 40000 q*8")
+    got, ref = _run(torch_cuda, 16, 2, 40000, seed=11, q_scale=8.0)
+    _check(got, ref, "sharp, long runs")
+
+
+def test_attention_graph_replay(torch_cuda):
+    """Three calls (different queries and caches) captured into one HIP graph and replayed
+    three times, with eager calls between the replays: every replay equals the eager result."""
+    torch = torch_cuda
+    d, ctx = 128, 9000
+    shp = L.gqa_shape(16, 2, d, ctx)
+    nbytes = L.moe_gqa_decode_workspace_bytes(shp)
+    ins = []
+    for s_ in range(3):
+        q, k, v = wl.make_attention_inputs(16, 2, d, ctx, seed=20 + s_)
+        ins.append((dev.to_device(q), dev.to_device(k), dev.to_device(v)))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((16, d), dtype=torch.int16, device="cuda") for _ in range(3)]
+    ref = []
+    for (qd, kd, vd), o in zip(ins, outs):
+        L.moe_gqa_decode_attention(shp, qd, kd, vd, o, ws)
+        ref.append(o.clone())
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for (qd, kd, vd), o in zip(ins, outs):
+            L.moe_gqa_decode_attention(shp, qd, kd, vd, o, ws, stream=side)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for (qd, kd, vd), o in zip(ins, outs):
+            L.moe_gqa_decode_attention(shp, qd, kd, vd, o, ws, stream=cap)
+    other = torch.empty((16, d), dtype=torch.int16, device="cuda")
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(outs[i], ref[i]), f"replay {rep}, call {i}"
+        # eager work between the replays (it reuses the workspace)
+        qd, kd, vd = ins[rep]
+        L.moe_gqa_decode_attention(shp, qd, kd, vd, other, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref[rep])
+    del g
