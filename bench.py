@@ -58,8 +58,8 @@ KERNEL_LABEL = {
 # taken on is named in the matching profiles/ summary.  A workload missing here reports
 # traffic null.
 TRAFFIC = {
-    # commit a62cd4d (profiles/grouped_gemms_pair_prefill512_traffic.md)
-    "prefill512": {"fetch_kib": 248885.8, "write_kib": 27770.9,
+    # commit b94ebe5 (profiles/grouped_gemms_pair_prefill512_traffic.md)
+    "prefill512": {"fetch_kib": 248694.3, "write_kib": 27782.2,
                    "copy_fetch_kib": 524300.0, "copy_write_kib": 1048576.0,
                    "copy_bytes": 1 << 30},
 }
