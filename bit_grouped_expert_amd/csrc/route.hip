@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
   float acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-  constexpr int UN = TT <= 4 ? 4 : 2;  // steps whose loads are in flight together
+  constexpr int UN = TT <= 4 ? 8 : 2;  // steps whose loads are in flight together (d_model 2048 in one round)
   for (int k0 = 0; k0 < D; k0 += 256 * UN) {
     f32x4_t rv[UN];
     u32x2_t xw[UN][TT];
