@@ -424,6 +424,19 @@ def test_layer_forward_parity_full(torch_cuda, name):
     _layer_full_check(torch_cuda, cfg)
 
 
+@pytest.mark.parametrize("routing", ["natural", "zipf"])
+def test_layer_forward_paired_multi_tile_groups(torch_cuda, routing):
+    """1000 tokens (about 31 rows per expert on average, still the resident engine): the
+    paired gate_up/down launch with groups of more than 32 rows (two or more tiles each, so
+    a tile's down work waits on gate_up chunks of several workgroups), with natural and
+    Zipf-skewed routing (empty groups, one group of hundreds of rows), every element."""
+    cfg = wl.MoEConfig(f"paired1000_{routing}", 1000, 2048, 256, 8, 512, routing=routing)
+    plan = L.moe_layer_plan(L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F))
+    assert plan.gemm_engine == L.MOE_ENGINE_RESIDENT and plan.paired == 1
+    say(f"layer {cfg.name}: full oracle (paired launch)")
+    _layer_full_check(torch_cuda, cfg)
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_layer_forward_parity_engines(torch_cuda, name, engine):
