@@ -20,7 +20,10 @@ system-scope fence of a default event) and of the whole layer, the same for the 
 layer, a measured HBM ceiling (a plain device copy and a streaming read, timed with events)
 and the CPU oracle's rate on a bounded sample.  The per-stage breakdown (stage_us) comes
 from a separate pass after each timed region with an event at every stage boundary, since
-those events themselves cost a few microseconds per step.
+those events themselves cost a few microseconds per step; the per-call latency
+distribution (latency: p10 / p50 / p90) from another pass with one event before and one
+after each call.  `staged_ablation` times the same layer through the staged entry points,
+with the group offsets kept on the device and with the host reading them back.
 
     python bench.py [--steps K] [--warmup W] [--config prefill512|zipf8192|uniform8192|...]
                     [--no-secondary] [--no-decode] [--no-long] [--no-attention]
@@ -45,6 +48,7 @@ RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 METRIC = "MoE-layer tokens/sec at T=512 and T=8192; % of HBM / MFMA roofline"
 SECONDARY = "zipf8192"          # the T=8192 half of the metric, measured in the same run
 EV_EVERY = 4                    # timed steps per pair of events around the dominant launch
+N_LAT = 100                     # calls in the per-call latency pass (p10 / p50 / p90)
 
 # the dominant kernel for each workload: the grouped gate_up (wide-tile engine), or, where
 # the library runs gate_up and down as one launch (moe_layer_plan: paired), that launch
@@ -73,8 +77,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    # the first ~100 layer calls of a process run a few percent slower (measured: 166 against
+    # 160 us per layer at 512 tokens right after 50 warm-up calls), so the default warm-up
+    # is longer than that
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default="prefill512")
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-attention", action="store_true",
@@ -183,11 +190,12 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     paired = bool(plan.paired)
     eng = {L.MOE_ENGINE_WIDE: "wide", L.MOE_ENGINE_RESIDENT: "resident"}.get(plan.gemm_engine)
     n_brk = min(steps, 20)
-    evs = [[dev.hip_event() for _ in range(nst)] for _ in range(steps)]
-    brk = [[dev.hip_event() for _ in range(nst)] for _ in range(n_brk)]
-    opts_gu = [L.layer_opts("auto", [e if j in (GU, GU + 1) else None for j, e in enumerate(row)])
-               for row in evs]
-    opts_all = [L.layer_opts("auto", row) for row in brk]
+    # events exist only while their pass runs (each pass creates and destroys its own): the
+    # timed steps that record the two events around the dominant launch
+    sampled = [i for i in range(steps) if i % EV_EVERY == 0]
+    evs = {i: (dev.hip_event(), dev.hip_event()) for i in sampled}
+    opts_gu = {i: L.layer_opts("auto", [a if j == GU else b if j == GU + 1 else None for j in range(nst)])
+               for i, (a, b) in evs.items()}
 
     def step(i, opts=None):
         lw = sets[i % len(sets)]
@@ -204,19 +212,41 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     # ---- timed region: exactly K steps; every EV_EVERY-th step (the first included) records
     # the two events around the dominant launch (an event costs about a microsecond of
     # stream time, so the others run without)
-    sampled = [i for i in range(steps) if i % EV_EVERY == 0]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, opts_gu[i] if i % EV_EVERY == 0 else None)
+        step(i, opts_gu.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / steps
-    gu_ms = float(np.mean([dev.hip_elapsed_ms(evs[i][GU], evs[i][GU + 1]) for i in sampled]))
+    gu_ms = float(np.mean([dev.hip_elapsed_ms(a, b) for a, b in evs.values()]))
+    for a, b in evs.values():
+        dev.hip_event_destroy(a)
+        dev.hip_event_destroy(b)
     log(f"bench: {cfg.name}: {steps} steps in {elapsed * 1e3:.2f} ms ({ms_per_step:.4f} ms/step), "
         f"{'gate_up + down (one launch)' if paired else 'gate_up'} {gu_ms * 1e3:.1f} us")
 
+    # ---- per-call latency distribution (reporting only), right after the timed region:
+    # N_LAT calls, each between one event before its first kernel and one after its last
+    # (an event's own cost, one to two microseconds of stream time, is inside every figure)
+    lat = [[dev.hip_event() for _ in range(2)] for _ in range(N_LAT)]
+    opts_lat = [L.layer_opts("auto", [a] + [None] * (nst - 2) + [b]) for a, b in lat]
+    for i in range(N_LAT):
+        step(i, opts_lat[i])
+    torch.cuda.synchronize()
+    lat_us = np.array([dev.hip_elapsed_ms(a, b) * 1e3 for a, b in lat])
+    p10, p50, p90 = (float(v) for v in np.percentile(lat_us, [10, 50, 90]))
+    latency = {"calls": N_LAT, "p10_us": p10, "p50_us": p50, "p90_us": p90,
+               "tokens_per_s_at_p50": cfg.T / (p50 * 1e-6)}
+    log(f"bench: {cfg.name}: per-call latency over {N_LAT} calls: p10 {p10:.1f} us, p50 {p50:.1f} us, "
+        f"p90 {p90:.1f} us")
+    for a, b in lat:
+        dev.hip_event_destroy(a)
+        dev.hip_event_destroy(b)
+
     # ---- per-stage breakdown (reporting only, outside the timed region)
+    brk = [[dev.hip_event() for _ in range(nst)] for _ in range(n_brk)]
+    opts_all = [L.layer_opts("auto", row) for row in brk]
     for i in range(n_brk):
         step(i, opts_all[i])
     torch.cuda.synchronize()
@@ -227,7 +257,8 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
                 for j, n in enumerate(names) if n}
     log(f"bench: {cfg.name}: breakdown (events at every stage): "
         + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in stage_ms.items()))
-    for row in evs + brk:
+
+    for row in brk:
         for e in row:
             dev.hip_event_destroy(e)
 
@@ -256,11 +287,72 @@ def measure(cfg, sets, steps, warmup, torch, L, dev, wl):
     return {
         "ms_per_step": ms_per_step, "value": cfg.T / (ms_per_step * 1e-3),
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "latency": latency,
         "touched_groups": touched,
         "rows_per_group": {"min": int(counts.min()), "median": float(np.median(counts)),
                            "max": int(counts.max()), "empty": int((counts == 0).sum())},
         "roofline": roof, "layer_roofline": layer,
     }, (x, router)
+
+
+def measure_staged(cfg, sets, torch, L, dev, wl, calls=40):
+    """The layer through the staged entry points (moe_route, moe_permute, four
+    moe_grouped_gemm_q4 calls: routed gate_up + SwiGLU, routed down, shared gate_up + SwiGLU,
+    shared down; moe_combine), every one on the stream with the group offsets on the device,
+    and the same chain with the host reading the offsets back between the permutation and
+    the GEMMs (a device-to-host copy and a stream synchronisation, as a host-sized launch
+    would need): the analogue of the pages' host-synchronisation ablation.  Per-layer times
+    are wall-clock over `calls` layers bracketed by synchronisations, rotating the weight
+    sets."""
+    T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
+    x, router = wl.make_activations(cfg, 0)
+    xd, rd = dev.to_device(x), dev.to_device(router)
+    shp = L.shape(T, D, E, k, F)
+    ws = dev.workspace(shp)
+    i32, i16 = torch.int32, torch.int16
+    idx = torch.empty((T, k), dtype=i32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    off = torch.empty(E + 1, dtype=i32, device="cuda")
+    st = torch.empty(T * k, dtype=i32, device="cuda")
+    sr = torch.empty(T * k, dtype=i32, device="cuda")
+    off_sh = torch.tensor([0, T], dtype=i32, device="cuda")
+    act = torch.empty((T * k, F), dtype=i16, device="cuda")
+    y = torch.empty((T * k, D), dtype=i16, device="cuda")
+    s_act = torch.empty((T, F), dtype=i16, device="cuda")
+    S = torch.empty((T, D), dtype=i16, device="cuda")
+    out = torch.empty((T, D), dtype=i16, device="cuda")
+    gws_n = max(L.moe_grouped_gemm_q4_workspace_bytes(E, T * k, T, D),
+                L.moe_grouped_gemm_q4_workspace_bytes(E, T * k, T * k, F),
+                L.moe_grouped_gemm_q4_workspace_bytes(1, T, T, D),
+                L.moe_grouped_gemm_q4_workspace_bytes(1, T, T, F))
+    gws = torch.empty(max(gws_n, 256), dtype=torch.uint8, device="cuda")
+
+    def layer(i, host_sync):
+        lw = sets[i % len(sets)]
+        ex, sh = lw.experts, lw.shared
+        L.moe_route(shp, xd, rd, idx, wts, ws)
+        L.moe_permute(shp, idx, off, st, sr, ws)
+        if host_sync:
+            off.cpu()  # device-to-host copy: the host waits for the stream
+        L.moe_grouped_gemm_q4(E, T * k, 2 * F, D, xd, T, st, off, ex.gate_up, 1, act, gws)
+        L.moe_grouped_gemm_q4(E, T * k, D, F, act, T * k, None, off, ex.down, 0, y, gws)
+        L.moe_grouped_gemm_q4(1, T, 2 * F, D, xd, T, None, off_sh, sh.gate_up, 1, s_act, gws)
+        L.moe_grouped_gemm_q4(1, T, D, F, s_act, T, None, off_sh, sh.down, 0, S, gws)
+        L.moe_combine(shp, y, sr, wts, S, out)
+
+    res = {}
+    for name, hs in (("device_offsets", False), ("host_sync", True)):
+        for i in range(8):
+            layer(i, hs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(calls):
+            layer(i, hs)
+        torch.cuda.synchronize()
+        res[name + "_us_per_layer"] = (time.perf_counter() - t0) / calls * 1e6
+    log(f"bench: {cfg.name}: staged entry points {res['device_offsets_us_per_layer']:.1f} us per layer, "
+        f"with the host reading the offsets {res['host_sync_us_per_layer']:.1f} us")
+    return res
 
 
 def measure_decode(cfg, sets, torch, L, dev, wl, layers=200):
@@ -556,10 +648,18 @@ def main():
     if not args.no_secondary and scfg.name != cfg.name and \
             (scfg.D, scfg.E, scfg.F, scfg.bias) == (cfg.D, cfg.E, cfg.F, cfg.bias):
         # same weight sets (the weights do not depend on T), the 8192-token Zipf-routed batch
-        s_res, _ = measure(scfg, sets, args.steps, min(args.warmup, 20), torch, L, dev, wl)
+        s_res, _ = measure(scfg, sets, args.steps, min(args.warmup, 40), torch, L, dev, wl)
         secondary = {"workload": f"{scfg.name}: one MoE layer, T={scfg.T}, Zipf-skewed routing, "
                                  "same shape and weights",
-                     "steps": args.steps, "warmup": min(args.warmup, 20), **s_res}
+                     "steps": args.steps, "warmup": min(args.warmup, 40), **s_res}
+
+    staged = None
+    if not args.no_secondary:
+        staged = {"workload": f"{cfg.name} through the staged entry points (route, permute, four "
+                              "grouped GEMM calls, combine): offsets kept on the device, and read "
+                              "back by the host between the permutation and the GEMMs",
+                  "fused_layer_us": main_res["ms_per_step"] * 1e3,
+                  **measure_staged(cfg, sets, torch, L, dev, wl)}
 
     decode = None
     if not args.no_decode:
@@ -618,11 +718,13 @@ def main():
                    "T": cfg.T, "d_model": cfg.D, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.F,
                    "routing": cfg.routing, "parallelism": "single GPU"},
         "stage_us": main_res["stage_us"],
+        "latency": main_res["latency"],
         "touched_groups": main_res["touched_groups"],
         "rows_per_group": main_res["rows_per_group"],
         "roofline": main_res["roofline"],
         "layer_roofline": main_res["layer_roofline"],
         "zipf8192": secondary,
+        "staged_ablation": staged,
         "decode": decode,
         "long32768": long,
         "gqa_decode_attention": attention,
