@@ -10,8 +10,9 @@
 //
 // Split over the cache (the decode query is one row, so the work is the cache read):
 //   partial   about one workgroup per compute unit, each over a run of 128-position chunks of
-//             one KV head, two chunks' rows in flight.  A chunk's key and
-//             value rows go to LDS with direct 1 KB loads (whole lines); the value rows are
+//             one KV head.  A chunk's key and value rows (whole lines) go to LDS with
+//             direct loads when the run is one chunk, else through registers, loaded while
+//             the previous chunk is computed; the value rows are
 //             transposed on the matrix cores (a product with identity slices, exact) into a
 //             second LDS copy; the group's query rows sit in registers.  Scores S = Q K^T on the matrix cores (the group's heads are the
 //             rows, padded to 16), the chunk's softmax numerators exp(s - m) with its max m
@@ -53,6 +54,10 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// 16-byte pieces of one chunk per lane: kPieces key and kPieces value pieces (1 KB per
+// wavefront each)
+constexpr int kPieces = (kC * 16 / 64) / kWaves;
+
 // vmcnt(n) with the other counters at their maximum (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8)
 template <int N>
@@ -64,13 +69,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-// loads of one chunk per wavefront: 4 x (key, value) direct loads of 1 KB
-constexpr int kLoadsPerChunk = 2 * (kC * 16 / 64) / kWaves;
-
-// Workgroup (x, g): chunks x * per_part .. of KV head g, two buffers, the next chunk's key
-// and value rows in flight while the current one is computed; the chunks are combined with
+// Workgroup (x, g): chunks x * per_part .. of KV head g, two buffers.  With one chunk per
+// workgroup (DIRECT) its key and value rows go straight to LDS (direct loads).  With more,
+// every chunk is loaded into registers while the one before it is computed and stored to
+// LDS at that chunk's end: the barriers inside the loop order LDS traffic only, so those
+// loads stay in flight across them (direct loads would not: the compiler waits for every
+// outstanding one before the first LDS read that follows, in every iteration, once the
+// kernel has issued any).  The chunks are combined with
 // a running maximum per head (O and the sum rescaled when it rises), so the workgroup
 // writes one partial.
+template <bool DIRECT>
 __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams p) {
   // per buffer: key rows (permuted chunks) for the scores, then the transposed value rows;
   // the value rows
@@ -91,19 +99,43 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-  // key and value rows of chunk c into buffer b: load I fills LDS bytes 1024 I ..
-  // (positions 4 I .. 4 I + 3); the 16-byte chunk ch of position r sits at slot
+  // key and value rows of chunk c: piece j of this lane is 16-byte slot I * 64 + l of the
+  // chunk's rows, I = wave + kWaves j (positions 4 I .. 4 I + 3), stored at LDS bytes
+  // 1024 I + 16 l of the buffer; the 16-byte chunk ch of position r sits at slot
   // ch ^ (r % 16), so that the sixteen positions a matrix-core step reads fall in distinct
   // bank groups.  Positions past the cache read the last cached row (finite values; their
   // weights are zero).
-  auto issue = [&](int c, int b) __attribute__((always_inline)) {
+  u32x4_t kr[kPieces], vr[kPieces];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
     const int pos0 = c * kC;
     const int npos = p.ctx - pos0 < kC ? p.ctx - pos0 : kC;
-    for (int I = wave; I < kC * 16 / 64; I += kWaves) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int I = wave + kWaves * j;
+      const int Gc = I * 64 + l, r = Gc >> 4, slot = Gc & 15;
+      const int64_t off = (int64_t)(pos0 + (r < npos ? r : npos - 1)) * kD + 8 * (slot ^ (r & 15));
+      kr[j] = *(const u32x4_t*)(kb + off);
+      vr[j] = *(const u32x4_t*)(vb + off);
+    }
+  };
+  auto put_direct = [&](int c, int b) __attribute__((always_inline)) {
+    const int pos0 = c * kC;
+    const int npos = p.ctx - pos0 < kC ? p.ctx - pos0 : kC;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int I = wave + kWaves * j;
       const int Gc = I * 64 + l, r = Gc >> 4, slot = Gc & 15;
       const int64_t off = (int64_t)(pos0 + (r < npos ? r : npos - 1)) * kD + 8 * (slot ^ (r & 15));
       __builtin_amdgcn_global_load_lds(kb + off, kv[b] + 1024 * I, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vb + off, vs[b] + 1024 * I, 16, 0, 0);
+    }
+  };
+  auto put = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int I = wave + kWaves * j;
+      *(u32x4_t*)(kv[b] + 1024 * I + 16 * l) = kr[j];
+      *(u32x4_t*)(vs[b] + 1024 * I + 16 * l) = vr[j];
     }
   };
   // the group's query rows as matrix-core A fragments: lane (head m, quarter q), dims
@@ -113,8 +145,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     qa[s] = m < G ? *(const u32x4_t*)(p.q + (h0 + m) * kD + 32 * s + 8 * q) : zero4;
-  issue(c_first, 0);
-  if (c_first + 1 < c_last) issue(c_first + 1, 1);
+  if constexpr (DIRECT) {
+    put_direct(c_first, 0);  // c_last == c_first + 1 (host-chosen)
+    wait_vmcnt<0>();
+  } else {
+    fetch(c_first);
+    put(0);
+    if (c_first + 1 < c_last) fetch(c_first + 1);
+  }
 
   // the value-transposing identity slices: with A = the wavefront's 16 positions x 32 dims
   // (lane (position m, quarter q) holds dims 32 s + 8 q .. + 7) and B = the 32 x 16 slice t
@@ -144,10 +182,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
   const int dcol = 16 * wave + m;
   for (int c = c_first; c < c_last; ++c) {
     const int b = (c - c_first) & 1;
-    // this chunk's rows have landed (only the next chunk's loads may still be in flight)
-    if (c + 1 < c_last) wait_vmcnt<kLoadsPerChunk>();
-    else wait_vmcnt<0>();
-    __syncthreads();
+    // this chunk's rows are in buffer b (the next chunk's loads may still be in flight)
+    lds_barrier();
     const int pos0 = c * kC;
     const int npos = p.ctx - pos0 < kC ? p.ctx - pos0 : kC;
     const unsigned char* kvb = kv[b];
@@ -180,7 +216,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
 #pragma unroll
       for (int i = 0; i < 4; ++i) red_m[wave][4 * q + i] = mx[i];
     }
-    __syncthreads();  // also: every wavefront is past its key reads
+    lds_barrier();  // also: every wavefront is past its key reads
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -211,7 +247,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
       ph[(4 * q + i) * kPRow + r] = hi;
       pl[(4 * q + i) * kPRow + r] = lo;
     }
-    __syncthreads();
+    lds_barrier();
     // O = alpha O + P V: wavefront w takes dims 16 w .. 16 w + 15 (B columns), the heads A rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -229,9 +265,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gqa_partial_kernel(AttnParams 
       const u32x4_t bv = *(const u32x4_t*)(kv[b] + dcol * kVtRow + 2 * pp);
       O = mfma16x16x32(al, bv, mfma16x16x32(ah, bv, O));
     }
+    // the next chunk to buffer b ^ 1 (last read in the previous chunk, before this chunk's
+    // first barrier), then the loads of the one after it
+    if (!DIRECT && c + 1 < c_last) put(b ^ 1);
+    if (!DIRECT && c + 2 < c_last) fetch(c + 2);
     // every wavefront is done with buffer b, P and the per-wavefront maxima and sums
-    __syncthreads();
-    if (c + 2 < c_last) issue(c + 2, b);
+    lds_barrier();
   }
   // O[i]: head 4 q + i, dim dcol
   const int64_t base = ((int64_t)g * p.n_part + x) * G;
@@ -358,7 +397,10 @@ void attn_partition(AttnParams* p, int n_cu) {
 }
 
 void launch_attention(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(gqa_partial_kernel, dim3(p.n_part, p.n_kv), dim3(64 * kWaves), 0, s, p);
+  if (p.per_part == 1)
+    hipLaunchKernelGGL(gqa_partial_kernel<true>, dim3(p.n_part, p.n_kv), dim3(64 * kWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL(gqa_partial_kernel<false>, dim3(p.n_part, p.n_kv), dim3(64 * kWaves), 0, s, p);
   hipLaunchKernelGGL(gqa_reduce_kernel, dim3(p.n_q, kD / kRedDims), dim3(kRedSlices * kRedDims), 0,
                      s, p);
 }

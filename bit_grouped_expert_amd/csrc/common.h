@@ -83,6 +83,27 @@ __device__ __forceinline__ uint32_t ldg_u32(const void* p) {
   return __builtin_nontemporal_load((const uint32_t*)p);
 }
 
+// s_waitcnt vmcnt(0) with the other counters unconstrained, fenced against reordering
+__device__ __forceinline__ void wait_vmcnt0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations only, not
+// for its in-flight global loads (__syncthreads() is a workgroup fence as well, and waits
+// for every outstanding vector-memory operation, so a prefetch issued before it is drained
+// at the barrier).  Enough wherever the barrier orders LDS accesses between the
+// workgroup's threads and no global-memory access of one thread must be seen by another.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 // Device-scope (agent) accesses, coherent across the XCDs' L2 caches: what one
 // workgroup writes this way and another reads this way within one launch is seen once a
 // completed store is followed by a counter or flag that the reader observes.

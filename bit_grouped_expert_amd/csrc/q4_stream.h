@@ -32,24 +32,6 @@ __device__ __forceinline__ T ld(const void* base, uint32_t byte_off) {
   return *(const T*)((const char*)base + byte_off);
 }
 
-// s_waitcnt vmcnt(0) with the other counters unconstrained, fenced against reordering
-__device__ __forceinline__ void wait_vmcnt0() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations only,
-// not for its in-flight weight loads (a __syncthreads() would drain those).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
 // natural column c (0..7) of an 8-column run -> its position in the order 0,4,1,5,...
 __device__ __forceinline__ int perm8(int c) { return ((c & 3) << 1) | (c >> 2); }
 
