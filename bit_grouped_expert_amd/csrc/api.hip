@@ -83,7 +83,7 @@ int device_cu_count() {
 
 struct Layout {
   size_t rsplit, logits, topk_idx, topk_w, chunk_cnt, offsets, sorted_tok, slot_row, tiles,
-      tile_count, xsum_x, xsum_act, xprep, act, y, sync, dec_part, dec_act, total;
+      tile_count, xsum_x, xsum_act, xprep, act, y, sync, dec_part, dec_act, dec_plan, total;
   int32_t sync_words;  // cleared by the routing kernels of every call
 };
 
@@ -131,11 +131,12 @@ Layout make_layout(const moe_shape* s) {
   }
   L.sync_words = (int32_t)words;
   L.sync = take((size_t)words * 4);
-  L.dec_part = L.dec_act = 0;
+  L.dec_part = L.dec_act = L.dec_plan = 0;
   if (decode_ok(s)) {
     const int ms = (int)decode_max_slots(s);
     L.dec_part = take(decode_part_bytes((int)D, (int)F, ms));
     L.dec_act = take(decode_act_bytes((int)F, ms));
+    L.dec_plan = take(decode_plan_bytes());
   }
   L.total = o;
   return L;
@@ -589,6 +590,10 @@ static moe_status layer_impl(const moe_shape* shape, const uint16_t* x, const fl
     dp.sync = sync;
     dp.part = at<float>(ws, L.dec_part);
     dp.act = at<uint16_t>(ws, L.dec_act);
+    dp.plan = at<uint32_t>(ws, L.dec_plan);
+    // two workgroups per compute unit are resident at once: the later ones take the
+    // plan workgroup 0 publishes
+    dp.early = 2 * device_cu_count();
     dp.out = out;
     dp.up_main = q4p(experts->gate_up);
     dp.down_main = q4p(experts->down);

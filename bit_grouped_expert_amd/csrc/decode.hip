@@ -74,7 +74,12 @@ static_assert(kGroupSlots <= 16, "pair scan width");
 // done flag per gate_up item, slot-major, set by a plain store.  Many atomics on one line
 // serialise at the memory, so nothing is counted that way on the critical path.
 constexpr int kSyncCb = 32;
+constexpr int kSyncPlan = 1;  // [1]: workgroup 0 has published the plan
 __host__ __device__ inline int sync_flags_base(int n_cb) { return kSyncCb + 32 * n_cb; }
+
+// the published plan (32-bit words): n_slots, slot_exp, rowmask, then coef
+constexpr int kPubExp = 1, kPubMask = kPubExp + kDecodeMaxSlots, kPubCoef = kPubMask + kDecodeMaxSlots;
+constexpr int kPubWords = kPubCoef + kDecodeMaxSlots * 16;
 
 // the plan, in LDS, identical in every workgroup
 struct Plan {
@@ -87,6 +92,7 @@ struct Plan {
   uint32_t rowmask[kDecodeMaxSlots];  // tokens of each slot
   int n_slots;
   int last;  // a down item completes its column block
+  int pub_ok;  // the published plan was there
   // a down item's (slot, token) pairs: pair j of the group's slot b is pbase[b] + j, and
   // prow[pair] is its activation row (slot * 16 + token)
   int pbase[kGroupSlots + 1];
@@ -231,6 +237,49 @@ __device__ void make_plan(const DecodeParams& p, Plan& pl, bool writer) {
     }
   }
   __syncthreads();
+}
+
+// Workgroup 0 publishes the parts of the plan the items read (device-scope stores, complete
+// before the flag is raised); a workgroup of a later round waits for the flag (bounded: if
+// it does not come, the workgroup computes the plan itself) and loads them.
+__device__ void publish_plan(const DecodeParams& p, const Plan& pl) {
+  const int tid = threadIdx.x, n = pl.n_slots;
+  for (int i = tid; i < n; i += kThreads) {
+    store_dev(p.plan + kPubExp + i, (uint32_t)pl.slot_exp[i]);
+    store_dev(p.plan + kPubMask + i, pl.rowmask[i]);
+  }
+  for (int i = tid; i < n * 16; i += kThreads) store_dev(p.plan + kPubCoef + i, __float_as_uint(pl.coef[i]));
+  if (tid == 0) store_dev(p.plan, (uint32_t)n);
+  wait_vmcnt0();
+  __syncthreads();
+  if (tid == 0) store_dev((uint32_t*)(p.sync + kSyncPlan), 1u);
+}
+
+__device__ bool load_plan(const DecodeParams& p, Plan& pl) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int spins = 0, got = 0;
+    for (;;) {
+      if (__all(load_dev((const uint32_t*)(p.sync + kSyncPlan)) != 0u)) {
+        got = 1;
+        break;
+      }
+      if (++spins > kSpinLimit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (tid == 0) pl.pub_ok = got;
+  }
+  __syncthreads();
+  if (!pl.pub_ok) return false;  // the same in every thread
+  const int n = (int)load_dev(p.plan);
+  for (int i = tid; i < n; i += kThreads) {
+    pl.slot_exp[i] = (int)load_dev(p.plan + kPubExp + i);
+    pl.rowmask[i] = load_dev(p.plan + kPubMask + i);
+  }
+  for (int i = tid; i < n * 16; i += kThreads) pl.coef[i] = __uint_as_float(load_dev(p.plan + kPubCoef + i));
+  if (tid == 0) pl.n_slots = n;
+  __syncthreads();
+  return true;
 }
 
 // ------------------------------------------------------------------------------- gate_up
@@ -524,7 +573,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXC <
 void decode_layer_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) Plan pl;
   __shared__ __attribute__((aligned(16))) unsigned char area[kArea];
-  make_plan<MAXC>(p, pl, blockIdx.x == 0);
+  if ((int)blockIdx.x < p.early || !load_plan(p, pl)) make_plan<MAXC>(p, pl, blockIdx.x == 0);
+  if (blockIdx.x == 0 && p.early < (int)gridDim.x) publish_plan(p, pl);
   const int n_slots = pl.n_slots, NSL = p.F >> 4;
   const int n_up = n_slots * NSL;
   const int n_sg = (n_slots + p.group_slots - 1) / p.group_slots;
@@ -559,6 +609,8 @@ size_t decode_part_bytes(int D, int F, int max_slots) {
 }
 
 size_t decode_act_bytes(int F, int max_slots) { return (size_t)max_slots * 16 * F * 2; }
+
+size_t decode_plan_bytes() { return (size_t)kPubWords * 4; }
 
 void launch_decode_layer(const DecodeParams& p, int max_slots, hipStream_t s) {
   // the most items any routing can give; workgroups past the actual count return

@@ -215,8 +215,15 @@ struct DecodeParams {
   uint16_t* act;        // bf16 [max slots][16 tokens][F], prepared column order
   uint16_t* out;        // bf16 [T, D]
   Q4Ptrs up_main, up_last, down_main, down_last;  // experts [E, ...]; the shared expert
+  // Workgroups from index `early` on (those that start only once earlier ones finish) take
+  // the plan that workgroup 0 publishes to `plan` (decode_plan_bytes()) instead of
+  // computing it, when it is there within a bounded wait; set early to the grid size or
+  // more to have every workgroup compute it.
+  int32_t early;
+  uint32_t* plan;
 };
 bool decode_supported(int T, int D, int E, int k, int F);
+size_t decode_plan_bytes();
 int decode_group_slots(int F);
 int decode_sync_ints(int D, int F, int max_slots);
 size_t decode_part_bytes(int D, int F, int max_slots);
