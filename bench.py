@@ -616,8 +616,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the layer would shard by tokens or experts; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the layer "
+              "would shard by tokens, or by experts with an all-to-all of token rows each way)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
