@@ -10,7 +10,7 @@ Pages this follows (cited by title and section):
         grouped-query attention with 16 query heads and two KV heads, over a growing KV
         cache) and paragraph 8 (decode reads the key and value cache; several query heads
         share one KV head's rows, so each cached row is loaded once for all of them).
-Readings taken where the pages are silent (each also listed in the design notes): head
+Readings taken where the pages are silent: head
 dim 128 (d_model 2048 over 16 query heads); scaled dot-product attention, softmax over
 q . k / sqrt(head dim), then the weighted sum of value rows; query head h reads KV head
 h // (n_q / n_kv); the cache holds bf16 rows [KV head][position][head dim] and the query
