@@ -19,6 +19,10 @@
  *     address of moe_layer_forward_noalloc's scratch array, taken once per
  *     device under std::call_once), so calls on different streams with
  *     different buffers are thread-safe.
+ *   - Kernels whose workgroups wait on other workgroups (the paired GEMM launch,
+ *     the decode-sized chain) bound every wait.  Work on other streams can only
+ *     delay such a wait; one that outlasts its bound (milliseconds) gives up, and
+ *     word 0 of the workspace's sync counters (moe_ws_layout.sync) counts it.
  *   - Every compute call only enqueues work on `stream` (NULL = the legacy
  *     default stream) and never waits for the device; buffers must stay valid
  *     until the stream has passed the call.  No host synchronisation happens
