@@ -293,11 +293,11 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
 #pragma unroll
         for (int j = 0; j < NBE; ++j) {
           const double sum = sums[j];
-          if (j < nb && (ce[j] & 63) == lane) {
+          // selects over every slot (a branch per slot lets the compiler index the
+          // array by ce[j] >> 6, which moves it to scratch memory)
+          const bool hit = j < nb && (ce[j] & 63) == lane;
 #pragma unroll
-            for (int c = 0; c < MAXC; ++c)
-              if (c == (ce[j] >> 6)) exact[c] = sum;
-          }
+          for (int c = 0; c < MAXC; ++c) exact[c] = (hit && c == (ce[j] >> 6)) ? sum : exact[c];
         }
         nb = 0;
       };
@@ -334,11 +334,9 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
           my_e = best.e;
           my_v = Lt[best.e];
         }
-        if ((best.e & 63) == lane) {
+        const bool won = (best.e & 63) == lane;
 #pragma unroll
-          for (int c = 0; c < MAXC; ++c)
-            if (c == (best.e >> 6)) cand[c] = false;
-        }
+        for (int c = 0; c < MAXC; ++c) cand[c] = (won && c == (best.e >> 6)) ? false : cand[c];
       }
     }
   }
