@@ -330,9 +330,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ Lt,
           if (better(o, best)) best = o;
         }
         if (best.e >= E) best.e = 0;  // only with NaN logits (fewer than k candidates)
+        // its fp32 logit from the lane that holds it (best is the same on every lane)
+        float bv = 0.f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) bv = c == (best.e >> 6) ? val[c] : bv;
+        bv = __shfl(bv, best.e & 63);
         if (lane == j) {
           my_e = best.e;
-          my_v = Lt[best.e];
+          my_v = bv;
         }
         const bool won = (best.e & 63) == lane;
 #pragma unroll
