@@ -283,6 +283,19 @@ def test_route_exact_ties(torch_cuda, E, k, T, D):
     _check_route(cfg, x, router, gi, gw)
 
 
+@pytest.mark.parametrize("T,D,E,k", [(2500, 192, 40, 4), (2100, 512, 200, 6), (2050, 256, 300, 5)])
+def test_route_many_tokens_off_shapes(torch_cuda, T, D, E, k):
+    """The many-token routers away from the layer's shape: d_model not a multiple of 256 (R
+    split once into bf16 planes, 64-token tiles of 32 experts), and multiples of 256 (the
+    64 x 128 tile kernel) with expert counts that leave a partial expert tile (up to 300
+    experts: the top-k's widest form) and token counts that leave a partial token tile."""
+    cfg = wl.MoEConfig("route_many", T, D, E, k, 64)
+    say(f"route T={T} D={D} E={E} k={k}")
+    x, router = wl.make_activations(cfg, 3)
+    gi, gw = _route_gpu(torch_cuda, cfg, x, router)
+    _check_route(cfg, x, router, gi, gw)
+
+
 # ----------------------------------------------------------------------------- permutation
 def _permute_gpu(torch, cfg, idx):
     shp = L.shape(cfg.T, cfg.D, cfg.E, cfg.k, cfg.F)
@@ -305,6 +318,23 @@ def test_permute_parity(torch_cuda, name):
     idx, _ = oracle.select_topk(oracle.router_logits(x, router), cfg.k)
     off, st, sr = _permute_gpu(torch_cuda, cfg, idx)
     r_off, r_st, r_sr = oracle.stable_permutation(idx, cfg.E)
+    assert np.array_equal(off, r_off)
+    assert np.array_equal(st, r_st)
+    assert np.array_equal(sr, r_sr)
+
+
+@pytest.mark.parametrize("T,E,k", [(2100, 300, 6), (1000, 1000, 4), (3000, 17, 3), (257, 257, 32)])
+def test_permute_off_shapes(torch_cuda, T, E, k):
+    """The standalone permutation's two forms away from the layer's shape (one workgroup per
+    four experts up to 8192 pairs and 1024 experts, count / scan / scatter beyond), on
+    seeded distinct expert ids per token, top_k up to 32: offsets, permuted tokens and rows
+    bit-exact."""
+    cfg = wl.MoEConfig("perm_off", T, 64, E, k, 64)
+    say(f"permute T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, st, sr = _permute_gpu(torch_cuda, cfg, idx)
+    r_off, r_st, r_sr = oracle.stable_permutation(idx, E)
     assert np.array_equal(off, r_off)
     assert np.array_equal(st, r_st)
     assert np.array_equal(sr, r_sr)
@@ -583,6 +613,24 @@ def test_layer_stage_events(torch_cuda):
     for e in evs:
         dev.hip_event_destroy(e)
     assert np.array_equal(dev.to_host(out, np.uint16), plain)
+
+
+@pytest.mark.parametrize("shape", [(2100, 512, 200, 6, 256), (3000, 256, 17, 3, 128)])
+def test_layer_many_tokens_off_shapes(torch_cuda, shape):
+    """Many-token layers away from the Qwen-like shape, every element against the oracle and
+    the routing outputs on every token: 200 experts (a partial 128-expert router tile),
+    12,600 pairs (count / scan / scatter), about 63 rows per group (128-row tiles); and 17
+    experts of about 530 rows with d_ff 128 (a down K below one 256-wide stage)."""
+    T, D, E, k, F = shape
+    cfg = wl.MoEConfig("many_off", T, D, E, k, F)
+    x, router = wl.make_activations(cfg, 21)
+    w = wl.make_weights(cfg, 77)
+    lw = dev.LayerWeights(w, cfg.E)
+    say(f"many-token layer {shape}")
+    got, inter = _layer_gpu(torch_cuda, cfg, x, router, lw)
+    _check_layer_integer_stages(cfg, x, router, inter)
+    ref = oracle.moe_layer(x, router, w, cfg.k)
+    check_tol(bf16f(got), ref["out"], f"many-token layer {shape}")
 
 
 # ----------------------------------------------------------------------------- decode sizes
