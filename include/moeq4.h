@@ -21,8 +21,11 @@
  *     different buffers are thread-safe.
  *   - Kernels whose workgroups wait on other workgroups (the paired GEMM launch,
  *     the decode-sized chain) bound every wait.  Work on other streams can only
- *     delay such a wait; one that outlasts its bound (milliseconds) gives up, and
- *     word 0 of the workspace's sync counters (moe_ws_layout.sync) counts it.
+ *     delay such a wait.  One that outlasts its bound (milliseconds) gives up:
+ *     a decode-chain workgroup waiting for the published routing plan then
+ *     computes the plan itself; any other such wait is counted in word 0 of the
+ *     workspace's sync counters (moe_ws_layout.sync), and that call's output is
+ *     not to be trusted.
  *   - Every compute call only enqueues work on `stream` (NULL = the legacy
  *     default stream) and never waits for the device; buffers must stay valid
  *     until the stream has passed the call.  No host synchronisation happens
