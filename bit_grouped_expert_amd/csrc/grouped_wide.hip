@@ -538,12 +538,6 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f < nfv) {
-        // the fragment's first output row, recomputed in each epilogue (the empty asm hides
-        // that it is the same every time): hoisted out of the block loop, the eight row
-        // addresses would hold sixteen registers through it and push others to scratch
-        int rowf = row0 + 16 * f;
-        asm volatile("" : "+s"(rowf));
-        uint16_t* crow = p.C + (int64_t)rowf * p.ldc;
         if (SWIGLU) {
           const int col = p.c_perm ? ((m & 8) | perm8(m & 7)) : m;
 #pragma unroll
@@ -554,7 +548,8 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
           const int r = l >> 1, half = l & 1;
           const int u = 8 * blk + wave;
           if (l < 32 && 16 * f + r < nrows)
-            *(u32x4_t*)(crow + (r * p.ldc + 16 * u + 8 * half)) = *(const u32x4_t*)(cs + r * 16 + 8 * half);
+            *(u32x4_t*)(p.C + (int64_t)(row0 + 16 * f + r) * p.ldc + 16 * u + 8 * half) =
+                *(const u32x4_t*)(cs + r * 16 + 8 * half);
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
@@ -562,7 +557,7 @@ __device__ __forceinline__ void wide_body(const WideParams& p, const WideLds& ld
             for (int i = 0; i < 4; ++i) cs[(4 * q + i) * 32 + 16 * j + m] = to_bf16(acc[f][j][i]);
           const int r = l >> 2, piece = l & 3;
           if (16 * f + r < nrows)
-            *(u32x4_t*)(crow + (r * p.ldc + 256 * blk + 32 * wave + 8 * piece)) =
+            *(u32x4_t*)(p.C + (int64_t)(row0 + 16 * f + r) * p.ldc + 256 * blk + 32 * wave + 8 * piece) =
                 *(const u32x4_t*)(cs + r * 32 + 8 * piece);
         }
       }
